@@ -1,0 +1,217 @@
+"""Benchmark of the fused routed + shared-expert MoE layer forward on one MI355X.
+
+One step = one whole layer forward (routing + gate dot + sort + stage 1 +
+stage 2 with the shared-expert addend) over one batch of seeded synthetic
+inputs already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
+                    [--mode auto|pseudo|aux|best] [--graph] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s and achieved TFLOPS (% MFMA peak) / GB/s (% HBM) on 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "a8w8": 5000.0}
+DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "a8w8": "fp8-e4m3"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--mode", default="best", choices=["auto", "pseudo", "aux", "best"])
+    ap.add_argument("--copies", type=int, default=0, help="weight copies rotated per step (0 = auto)")
+    ap.add_argument("--graph", action="store_true", help="time HIP-graph replays of the forward")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def algorithmic(cfg, ids, m_pseudo):
+    """Algorithmic FLOPs and bytes of the layer and of routed stage 1."""
+    import workloads
+    bw = workloads.bytes_per_weight(cfg.fmt)
+    bx = {"f32": 4, "bf16": 2, "mxfp8": 2, "a8w8": 1}[cfg.fmt]
+    bh = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32, "a8w8": 1}[cfg.fmt]
+    bo = 4 if cfg.fmt == "f32" else 2
+    T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.I_s, cfg.topk
+    P = T * k
+    active = int((np.bincount(ids.reshape(-1), minlength=cfg.E)[:cfg.E] > 0).sum())
+    flops = 6.0 * H * I * P + 6.0 * H * Is * T + (2.0 * H * T if cfg.gated else 0.0)
+    w_routed = active * 3.0 * H * I * bw
+    w_shared = 3.0 * H * Is * bw if Is else 0.0
+    # active routed weights once, shared weights once, x once, out once, logits,
+    # and the stage-1 output written and read once (routed and shared)
+    byt = (w_routed + w_shared + T * H * bx + T * H * bo + T * cfg.E * 4
+           + 2.0 * P * I * bh + 2.0 * T * Is * bh)
+    # stage 1 (routed + pseudo shared rows when fused): weights W13 once, x once, h written once
+    s1_w = active * 2.0 * H * I * bw + (2.0 * H * Is * bw if (Is and m_pseudo) else 0.0)
+    s1_bytes = s1_w + T * H * bx + (P + (T * m_pseudo if m_pseudo else 0)) * I * bh
+    s1_flops = 4.0 * H * I * P + (4.0 * H * Is * T if m_pseudo else 0.0)
+    return flops, byt, s1_flops, s1_bytes, active
+
+
+def cpu_baseline(cfg, inp, seconds):
+    """The oracle as it stands, on this host, over whole-layer passes of the
+    same workload (decode_bf16: all 32 tokens per pass) until ``seconds``."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    host = workloads.to_host(inp, lazy_weights=cfg.T * cfg.topk < cfg.E * 4)
+    tokens = np.arange(cfg.T)
+    if cfg.name == "a8w8_large" or cfg.name == "mxfp8" or cfg.name == "prefill_bf16":
+        tokens = np.arange(min(cfg.T, 16))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_layer(host, cfg, tokens=tokens)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample = f"{n} oracle passes over {tokens.size} tokens of {cfg.name} ({el:.1f} s)"
+    return {"value": n * tokens.size / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; --gpus N with N > 1 is not supported "
+                                   "(no collectives or sharding in this build)"}))
+        sys.exit(2)
+    import torch
+    import workloads
+    import routed_shared_experts_amd as m
+
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[args.workload]
+    inp = workloads.generate(cfg, device=dev)
+    wbytes = workloads.bytes_per_weight(cfg.fmt) * 3.0 * cfg.H * (cfg.E * cfg.I + cfg.I_s)
+    copies = args.copies or max(1, min(6, int(np.ceil(3 * 256e6 / wbytes))))
+    # rotate weight copies so the per-step footprint exceeds the 256 MB Infinity Cache
+    sets = [inp]
+    for _ in range(copies - 1):
+        c = dict(inp)
+        for k in ("w13", "w2", "ws13", "ws2", "w13_scale", "w2_scale", "ws13_scale", "ws2_scale"):
+            if inp.get(k) is not None:
+                c[k] = inp[k].clone()
+        sets.append(c)
+
+    modes = ["pseudo", "aux"] if args.mode == "best" else [args.mode]
+    results = {}
+    for mode in modes:
+        layers = [m.MoeLayer(cfg, s, shared_mode=mode) for s in sets]
+        out = layers[0].out
+        for L in layers[1:]:
+            L.args.out = m._ptr(out)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        stream = torch.cuda.current_stream()
+        for e in evs:
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            layers[i % copies].forward()
+        torch.cuda.synchronize()
+
+        if args.graph:
+            graphs = []
+            for L in layers:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    L.forward()
+                graphs.append(g)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % copies].replay()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            stage = None
+        else:
+            # live per-kernel timing: events at the step boundaries on the main stream
+            handles = []
+            for e in evs:
+                arr = (m.c_void_p * 5)(*[x.cuda_event for x in e])
+                handles.append(arr)
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                L = layers[i % copies]
+                L.args.timing_events = m.ctypes.cast(handles[i], m.c_void_p)
+                L.forward()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            for L in layers:
+                L.args.timing_events = None
+            names = ["prologue", "sort", "stage1", "stage2"]
+            stage = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                     for j, n in enumerate(names)}
+        results[mode] = (el, stage, layers[0])
+        del layers
+
+    best = min(results, key=lambda k: results[k][0])
+    el, stage, layer = results[best]
+    ms = el / args.steps * 1e3
+    # routing result of the timed workload (for the algorithmic byte count)
+    ids = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=dev)
+    m.moe_route(inp["logits"], ids, w, topk=cfg.topk, bias=inp.get("bias"), n_group=cfg.n_group,
+                topk_group=cfg.topk_group, group_score_topk=cfg.group_score_topk,
+                score=m.MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else m.MOE_SCORE_SOFTMAX,
+                renormalize=cfg.renormalize, routed_scaling_factor=cfg.routed_scaling_factor)
+    torch.cuda.synchronize()
+    m_pseudo = cfg.n_pseudo if best == "pseudo" else 0
+    flops, byt, s1_flops, s1_bytes, active = algorithmic(cfg, ids.cpu().numpy(), m_pseudo)
+    rec = {
+        "metric": METRIC,
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[cfg.fmt],
+        "data": "synthetic (seeded; random-init weights of the workload's shapes)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "I_s": cfg.I_s,
+                   "topk": cfg.topk, "score": cfg.score, "shared_mode": best, "weight_copies": copies,
+                   "graph": bool(args.graph), "active_experts": active},
+        "layer": {"tflops": flops / (ms * 1e-3) / 1e12, "gbps": byt / (ms * 1e-3) / 1e9,
+                  "frac_mfma": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.fmt],
+                  "frac_hbm": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "algorithmic_bytes": byt, "algorithmic_flops": flops},
+        "modes_ms": {k: v[0] / args.steps * 1e3 for k, v in results.items()},
+    }
+    if stage is not None:
+        s1_ms = stage["stage1"]
+        rec["kernels_ms"] = stage
+        rec["roofline"] = {"kernel": "gemm stage 1 (routed gate/up + SiLU-mul)", "bound": "hbm",
+                           "achieved": s1_bytes / (s1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": s1_bytes / (s1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                           "bytes_per_launch": s1_bytes, "flops_per_launch": s1_flops}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels: number-format conversions, the
+// fully specified float32 exp/sigmoid used for routing decisions, and
+// wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---- bfloat16 (stored as uint16_t bit patterns) ---------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Round-to-nearest-even; inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---- OCP e4m3fn -------------------------------------------------------------
+// The hardware converter rounds to nearest even but turns values past 448 into
+// NaN, so the input is saturated to +-448 first (RNE with saturation).
+__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  return pack2_e4m3(a, b) | (pack2_e4m3(c, d) << 16);
+}
+
+// ---- specified float32 exp / sigmoid -----------------------------------------
+// Every step is one correctly rounded IEEE float32 operation (no contraction):
+// clamp to [-80, 80]; n = rint(x * log2 e); Cody-Waite reduction with
+// LN2_HI = 45426/2^16 (exact products for |n| < 256) and LN2_LO = ln2 - LN2_HI;
+// degree-7 Taylor polynomial (coefficients 1/j!) by Horner with separate
+// multiply and add; scale by 2^n.  sigmoid(x) = 1 / (1 + exp(-x)).
+// The operators are written out here (not through helper functions) so that
+// the contract(off) pragma covers every multiply and add: helpers defined
+// elsewhere would carry their own contraction flags and fuse into FMAs.
+__device__ __forceinline__ float spec_exp(float x) {
+#pragma clang fp contract(off)
+  const float kLog2e = 1.44269504088896340736f;
+  const float kLn2Hi = 45426.0f / 65536.0f;
+  const float kLn2Lo = (float)(0.6931471805599453 - 45426.0 / 65536.0);
+  x = fminf(fmaxf(x, -80.0f), 80.0f);
+  const float n = __builtin_rintf(x * kLog2e);
+  const float t1 = n * kLn2Hi;
+  const float t2 = n * kLn2Lo;
+  const float r = (x - t1) - t2;
+  float p = (float)(1.0 / 5040.0);
+  p = p * r;
+  p = p + (float)(1.0 / 720.0);
+  p = p * r;
+  p = p + (float)(1.0 / 120.0);
+  p = p * r;
+  p = p + (float)(1.0 / 24.0);
+  p = p * r;
+  p = p + (float)(1.0 / 6.0);
+  p = p * r;
+  p = p + 0.5f;
+  p = p * r;
+  p = p + 1.0f;
+  p = p * r;
+  p = p + 1.0f;
+  return __builtin_ldexpf(p, (int)n);
+}
+__device__ __forceinline__ float spec_sigmoid(float x) {
+#pragma clang fp contract(off)
+  const float d = 1.0f + spec_exp(-x);
+  return 1.0f / d;  // correctly rounded fp32 division (HIP default)
+}
+
+// SiLU(g) * u for the stage-1 epilogue (ordinary accuracy is enough here).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---- wave64 reductions --------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Make this wave's LDS writes visible to its other lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is folded onto +0 so that equal values tie.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  f = f + 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+}  // namespace moe

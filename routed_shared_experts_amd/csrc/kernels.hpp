@@ -1,0 +1,80 @@
+// Internal launch interface between the host dispatcher (api.cpp) and the
+// gfx950 kernels.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Fmt : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX = 2, FMT_A8W8 = 3 };
+
+struct RouteParams {
+  const float* logits;
+  const float* bias;
+  int T, E, topk, n_group, topk_group, gtopk, score, renorm;
+  float scale;
+  int n_pseudo;
+  const float* gamma_in;  // pseudo-slot weights when the gate is not fused (or NULL)
+  int32_t* ids;
+  float* w;
+  // fused gate dot (gate_w != NULL)
+  const void* x;
+  int x_f32;  // 1: x/gate are fp32, 0: bf16
+  const void* gate_w;
+  int H;
+  float* gamma_out;
+  // fused MX quantisation of bf16 x (xq != NULL)
+  uint8_t* xq;
+  uint8_t* xs;
+  int do_route;
+};
+
+struct SortParams {
+  const int32_t* ids;
+  int P, n_experts, block_m, capacity;
+  int32_t* sorted;
+  int32_t* block_expert;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* num_blocks;
+  uint4* zero_ptr;
+  long long zero_vec;  // number of 16-byte vectors to clear
+};
+
+struct GemmParams {
+  int T, H, E, I, I_s, n_pseudo, k_total;
+  const uint8_t* w13;
+  const uint8_t* w2;
+  const void* w13_s;
+  const void* w2_s;
+  const uint8_t* ws13;
+  const uint8_t* ws2;
+  const void* ws13_s;
+  const void* ws2_s;
+  const uint8_t* x;
+  const void* x_s;
+  int dense, block_m, max_blocks;
+  const int32_t* sorted;
+  const int32_t* block_expert;
+  const int32_t* num_blocks;
+  uint8_t* h;
+  void* h_s;
+  int ld_h;
+  const float* pair_w;
+  const float* gamma;
+  float* acc;
+  void* out;
+  int out_bf16;
+  int mode;  // 0 store, 1 accumulate
+  int32_t* counters;
+  int expected;
+};
+
+hipError_t launch_route(const RouteParams& p, hipStream_t s);
+hipError_t launch_gate_dot(const void* x, int x_f32, const void* g, int T, int H, int apply_sigmoid,
+                           float* out, hipStream_t s);
+hipError_t launch_sort(const SortParams& p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s);
+
+}  // namespace moe
