@@ -159,16 +159,16 @@ moe_status moe_validate(const moe_forward_args* a);
 size_t moe_workspace_bytes(const moe_forward_args* a);
 
 /* The whole layer.  Launch sequence:
- *   PSEUDO/NONE: prologue (route + gate dot + MX quant of x) -> sort (zeroes
- *                the fp32 accumulator and counters) -> stage 1 -> stage 2
- *                (weighted scatter-add; the last arrival per (token, column
- *                tile) rounds once and writes out).
- *   AUX:         main records ev_fork; aux waits on it and runs the gate dot,
- *                dense shared stage 1 and shared stage 2 (STORE of gamma*S(x)
- *                into the accumulator), then records ev_ready.  Main runs the
- *                prologue, the sort (counters only, no accumulator zeroing),
- *                routed stage 1, waits on ev_ready on the device, then routed
- *                stage 2 accumulates onto the addend.
+ *   PSEUDO/NONE: prologue (route + gate dot + MX quant of x) -> sort (also
+ *                clears the arrival counters) -> stage 1 -> stage 2 (per-pair
+ *                rows; the last arrival per (token, column tile) sums them in
+ *                slot order and rounds once into out).
+ *   AUX:         main runs the prologue and records ev_fork; aux waits on it
+ *                and runs dense shared stage 1 and shared stage 2 (STORE of
+ *                gamma*S(x) into the addend buffer), then records ev_ready.
+ *                Main runs the sort and routed stage 1 concurrently, waits on
+ *                ev_ready on the device, then routed stage 2 sums the addend
+ *                and the routed pair rows.
  * workspace: device buffer of at least moe_workspace_bytes(a) bytes, 256-byte
  * aligned; its contents on entry are irrelevant.  main/aux: distinct streams
  * in AUX mode (aux ignored otherwise).  ev_fork/ev_ready: caller-created
@@ -218,23 +218,31 @@ moe_status moe_quant_mx(const void* x, int32_t T, int32_t H, uint8_t* codes,
  * rounded up to a multiple of block_m.  Host-only. */
 int32_t moe_sort_capacity(int32_t T, int32_t k_total, int32_t n_experts, int32_t block_m);
 
+/* Device scratch bytes moe_sort_tokens can use to sort large pair counts
+ * with three launches instead of one workgroup (0 when it would not use it).
+ * Host-only. */
+size_t moe_sort_scratch_bytes(int32_t T, int32_t k_total, int32_t n_experts);
+
 /* Token-by-expert sort (vLLM PR 65207, commit 2 and the review's sorting
  * experiment).  For pair p = t*k_total + j with expert topk_ids[p]:
  * counts[e] = number of pairs of expert e; offsets[e] = exclusive scan of the
  * counts padded to multiples of block_m (offsets has n_experts+1 entries);
  * sorted_pair_ids[offsets[e] + i] = i-th smallest pair index of expert e, the
- * padding slots hold T*k_total; block_expert[b] = expert of block b for
- * b < *num_blocks (entries past it are -1 up to capacity/block_m);
+ * padding slots and the tail up to capacity hold T*k_total; block_expert[b] =
+ * expert of block b for b < *num_blocks (-1 after it, up to capacity/block_m);
  * *num_blocks = offsets[n_experts] / block_m.  Empty experts get no block.
- * zero_ptr/zero_bytes (optional, zero_bytes % 16 == 0): a region cleared by the
- * same launch.  Arrays: sorted_pair_ids [capacity], block_expert
- * [capacity/block_m], counts [n_experts], offsets [n_experts+1].
- * Limits: n_experts <= 1024, T*k_total < 2^31. */
+ * scratch/scratch_bytes: optional device scratch of moe_sort_scratch_bytes()
+ * bytes (NULL: one workgroup sorts everything; same result, slower for large
+ * pair counts).  zero_ptr/zero_bytes (optional, zero_bytes % 16 == 0): a region
+ * cleared by the same launch.  Arrays: sorted_pair_ids [capacity],
+ * block_expert [capacity/block_m], counts [n_experts], offsets [n_experts+1].
+ * Limits: n_experts <= 576, T*k_total < 2^31. */
 moe_status moe_sort_tokens(const int32_t* topk_ids, int32_t T, int32_t k_total,
                            int32_t n_experts, int32_t block_m, int32_t capacity,
                            int32_t* sorted_pair_ids, int32_t* block_expert, int32_t* counts,
-                           int32_t* offsets, int32_t* num_blocks, void* zero_ptr,
-                           size_t zero_bytes, hipStream_t stream);
+                           int32_t* offsets, int32_t* num_blocks, void* scratch,
+                           size_t scratch_bytes, void* zero_ptr, size_t zero_bytes,
+                           hipStream_t stream);
 
 /* Arguments of the two GEMM stages.  Expert index e < E is routed expert e;
  * E <= e < E + n_pseudo is shared pseudo-expert p = e - E: rows
@@ -265,13 +273,15 @@ typedef struct {
   /* stage 2 */
   const float* pair_w; /* sorted: [T][k_total] pair weights (topk_w) */
   const float* gamma;  /* dense: [T] gate values or NULL (= 1) */
-  float* acc;          /* [T][H] fp32 accumulator */
+  float* acc;          /* STORE: [T][H] fp32 destination of gamma_t * S(x_t);
+                          ACCUMULATE: [T][H] fp32 addend, or NULL for none */
+  float* pair_out;     /* ACCUMULATE: [T*k_total][H] fp32, row t*k_total+j holds
+                          pair_w[t][j] * E_{e_tj}(x_t) (contents on entry irrelevant) */
   void* out;           /* [T][H] in out_dtype, written by the last arrival */
   int32_t out_dtype;
-  int32_t mode;        /* STORE: acc[t][:] = gamma_t * S(x_t) (dense only);
-                          ACCUMULATE: acc += w * E(x) then finalize */
-  int32_t* counters;   /* ACCUMULATE: [T][ceil(H/64)] int32, zero on entry */
-  int32_t expected_arrivals; /* contributions per token (k_total) */
+  int32_t mode;        /* STORE (dense only) or ACCUMULATE (sorted only) */
+  int32_t* counters;   /* ACCUMULATE: [T][H/64] int32, zero on entry */
+  int32_t expected_arrivals; /* contributions per token: must equal k_total */
   hipEvent_t addend_ready;   /* waited on (device-side) before stage 2, or NULL */
 } moe_stage_args;
 
@@ -284,11 +294,13 @@ typedef struct {
 moe_status moe_stage1(const moe_stage_args* a, hipStream_t stream);
 
 /* Stage 2 with the shared-expert addend accumulated in its epilogue (vLLM PR
- * 65207, "Purpose", commit 2): o = h . W2[e]^T in fp32 times the scales;
- * ACCUMULATE adds pair_w * o into acc[token] with fp32 atomics and the last
- * of expected_arrivals contributions to a (token, 64-column tile) rounds the
- * fp32 sum once into out; STORE writes gamma_t * o into acc (the addend).
- * Waits on addend_ready first when it is not NULL. */
+ * 65207, "Purpose", commit 2): o = h . W2[e]^T in fp32 times the scales.
+ * ACCUMULATE stores pair_w * o as the pair's row of pair_out; the last of the
+ * k_total contributions to a (token, 64-column tile) computes
+ * addend + sum_j pair_out[t*k_total + j] in fp32, j in slot order, and rounds
+ * it once into out (deterministic: the result does not depend on the order in
+ * which workgroups finish).  STORE writes gamma_t * o into acc (the addend of
+ * a later ACCUMULATE).  Waits on addend_ready first when it is not NULL. */
 moe_status moe_stage2_accum(const moe_stage_args* a, hipStream_t stream);
 
 /* Capability query (vLLM PR 65207, "Dependencies": the accumulate path is

@@ -34,7 +34,7 @@ SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE
 
 # Exported symbols, in the order of include/moe.h.
 EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_route", "shared_gate_dot",
-           "moe_quant_mx", "moe_sort_capacity", "moe_sort_tokens", "moe_stage1", "moe_stage2_accum",
+           "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_sort_tokens", "moe_stage1", "moe_stage2_accum",
            "moe_query_feature", "moe_status_str"]
 
 c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -63,7 +63,7 @@ class MoeStageArgs(ctypes.Structure):
                 ("block_m", c_int32), ("max_blocks", c_int32), ("sorted_pair_ids", c_void_p),
                 ("block_expert", c_void_p), ("num_blocks", c_void_p), ("h", c_void_p),
                 ("h_scale", c_void_p), ("pair_w", c_void_p), ("gamma", c_void_p), ("acc", c_void_p),
-                ("out", c_void_p), ("out_dtype", c_int32), ("mode", c_int32),
+                ("pair_out", c_void_p), ("out", c_void_p), ("out_dtype", c_int32), ("mode", c_int32),
                 ("counters", c_void_p), ("expected_arrivals", c_int32), ("addend_ready", c_void_p)]
 
 
@@ -89,8 +89,10 @@ def _load():
                                       c_void_p]),
         "moe_quant_mx": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "moe_sort_capacity": (c_int32, [c_int32, c_int32, c_int32, c_int32]),
+        "moe_sort_scratch_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
         "moe_sort_tokens": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
-                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
+                                      c_size_t, c_void_p]),
         "moe_stage1": (c_int32, [P(MoeStageArgs), c_void_p]),
         "moe_stage2_accum": (c_int32, [P(MoeStageArgs), c_void_p]),
         "moe_query_feature": (c_int32, [c_int32]),
@@ -170,13 +172,18 @@ def moe_quant_mx(x, codes, scales, stream=None):
     _check(st, "moe_quant_mx")
 
 
+def moe_sort_scratch_bytes(T, k_total, n_experts):
+    return int(_lib.moe_sort_scratch_bytes(T, k_total, n_experts))
+
+
 def moe_sort_tokens(topk_ids, n_experts, block_m, capacity, sorted_pair_ids, block_expert, counts, offsets,
-                    num_blocks, zero=None, stream=None):
+                    num_blocks, scratch=None, zero=None, stream=None):
     T, k_total = topk_ids.shape
     zb = 0 if zero is None else zero.numel() * zero.element_size()
+    sb = 0 if scratch is None else scratch.numel() * scratch.element_size()
     st = _lib.moe_sort_tokens(_ptr(topk_ids), T, k_total, n_experts, block_m, capacity, _ptr(sorted_pair_ids),
-                              _ptr(block_expert), _ptr(counts), _ptr(offsets), _ptr(num_blocks), _ptr(zero),
-                              zb, _stream(stream))
+                              _ptr(block_expert), _ptr(counts), _ptr(offsets), _ptr(num_blocks), _ptr(scratch),
+                              sb, _ptr(zero), zb, _stream(stream))
     _check(st, "moe_sort_tokens")
 
 

@@ -53,8 +53,8 @@ struct Plan {
   int m;     // pseudo experts
   int k_total, E_total, block_m, capacity, max_blocks;
   int dense_bm, dense_blocks;
-  size_t off_ids, off_w, off_gamma, off_xq, off_xs, off_counts, off_offsets, off_nblk, off_sorted,
-      off_bexp, off_h, off_hs, off_hsh, off_hshs, off_amax_sh, off_acc, off_cnt, off_amax, off_end;
+  size_t off_ids, off_w, off_gamma, off_xq, off_xs, off_counts, off_offsets, off_nblk, off_sorted, off_sortws,
+      off_bexp, off_h, off_hs, off_hsh, off_hshs, off_amax_sh, off_acc, off_pair, off_cnt, off_amax, off_end;
   size_t zero_begin, zero_end;  // region the sort launch clears
   size_t amax_sh_bytes;
 };
@@ -153,6 +153,7 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_offsets = take((size_t)(pl.E_total + 1) * 4);
   pl.off_nblk = take(16);
   pl.off_sorted = take((size_t)pl.capacity * 4);
+  pl.off_sortws = take(sort_scratch_bytes((int)P, pl.E_total));
   pl.off_bexp = take((size_t)pl.max_blocks * 4);
   pl.off_h = take((size_t)pl.capacity * a->I * esz_h);
   pl.off_hs = take(fmt == FMT_MX ? (size_t)pl.capacity * (a->I / 32) : 0);
@@ -162,12 +163,14 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_hshs = take(aux && fmt == FMT_MX ? dense_rows * (a->I_s / 32) : 0);
   pl.amax_sh_bytes = aux && fmt == FMT_A8W8 ? align_up(dense_rows * 4, kAlign) : 0;
   pl.off_amax_sh = take(pl.amax_sh_bytes);
-  // zeroed suffix: [acc][counters][row amax]; AUX mode leaves acc to the addend store
-  pl.off_acc = take((size_t)a->T * a->H * 4);
+  // the addend (AUX mode only) and the per-pair stage-2 rows
+  pl.off_acc = take(aux ? (size_t)a->T * a->H * 4 : 0);
+  pl.off_pair = take((size_t)P * a->H * 4);
+  // cleared by the sort launch: arrival counters, then the routed row amax (A8W8)
   pl.off_cnt = take((size_t)a->T * (a->H / 64) * 4);
   pl.off_amax = take(fmt == FMT_A8W8 ? (size_t)pl.capacity * 4 : 0);
   pl.off_end = o;
-  pl.zero_begin = aux ? pl.off_cnt : pl.off_acc;
+  pl.zero_begin = pl.off_cnt;
   pl.zero_end = o;
   return pl;
 }
@@ -241,6 +244,11 @@ int32_t moe_sort_capacity(int32_t T, int32_t k_total, int32_t n_experts, int32_t
 
 moe_status moe_validate(const moe_forward_args* a) { return validate_impl(a, nullptr); }
 
+size_t moe_sort_scratch_bytes(int32_t T, int32_t k_total, int32_t n_experts) {
+  if (T <= 0 || k_total <= 0 || n_experts <= 0) return 0;
+  return sort_scratch_bytes(T * k_total, n_experts);
+}
+
 size_t moe_workspace_bytes(const moe_forward_args* a) {
   int fmt = -1;
   if (validate_impl(a, &fmt) != MOE_OK) return 0;
@@ -313,7 +321,8 @@ moe_status moe_quant_mx(const void* x, int32_t T, int32_t H, uint8_t* codes, uin
 moe_status moe_sort_tokens(const int32_t* topk_ids, int32_t T, int32_t k_total, int32_t n_experts,
                            int32_t block_m, int32_t capacity, int32_t* sorted_pair_ids,
                            int32_t* block_expert, int32_t* counts, int32_t* offsets,
-                           int32_t* num_blocks, void* zero_ptr, size_t zero_bytes, hipStream_t stream) {
+                           int32_t* num_blocks, void* scratch, size_t scratch_bytes, void* zero_ptr,
+                           size_t zero_bytes, hipStream_t stream) {
   if (!topk_ids || !sorted_pair_ids || !block_expert || !counts || !offsets || !num_blocks)
     return MOE_ERR_INVALID_ARG;
   if (T <= 0 || k_total <= 0 || n_experts <= 0 || n_experts > kMaxSortExperts || block_m <= 0)
@@ -322,7 +331,11 @@ moe_status moe_sort_tokens(const int32_t* topk_ids, int32_t T, int32_t k_total, 
   if (capacity < moe_sort_capacity(T, k_total, n_experts, block_m) || capacity % block_m)
     return MOE_ERR_INVALID_ARG;
   if (zero_bytes % 16 || (zero_bytes && (!zero_ptr || !aligned16(zero_ptr)))) return MOE_ERR_INVALID_ARG;
+  const size_t need = sort_scratch_bytes(T * k_total, n_experts);
+  if (scratch && scratch_bytes < need) return MOE_ERR_WORKSPACE;
+  if (scratch && ((uintptr_t)scratch & 3u)) return MOE_ERR_INVALID_ARG;
   SortParams p{};
+  p.chunk_base = (scratch && need) ? static_cast<int32_t*>(scratch) : nullptr;
   p.ids = topk_ids;
   p.P = T * k_total;
   p.n_experts = n_experts;
@@ -380,6 +393,7 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   g.pair_w = a->pair_w;
   g.gamma = a->gamma;
   g.acc = a->acc;
+  g.pair_out = a->pair_out;
   g.out = a->out;
   g.out_bf16 = a->out_dtype == MOE_BF16;
   g.mode = a->mode;
@@ -402,11 +416,14 @@ moe_status moe_stage2_accum(const moe_stage_args* a, hipStream_t stream) {
   int fmt;
   moe_status st = stage_params(a, g, fmt);
   if (st != MOE_OK) return st;
-  if (!a->acc || !aligned16(a->acc)) return MOE_ERR_INVALID_ARG;
+  if (a->acc && !aligned16(a->acc)) return MOE_ERR_INVALID_ARG;
   if (a->mode == MOE_STAGE2_STORE) {
     if (!a->dense) return MOE_ERR_UNSUPPORTED;
+    if (!a->acc) return MOE_ERR_INVALID_ARG;
   } else if (a->mode == MOE_STAGE2_ACCUMULATE) {
-    if (!a->out || !a->counters || a->expected_arrivals <= 0 || (!a->pair_w && !a->dense)) return MOE_ERR_INVALID_ARG;
+    if (a->dense) return MOE_ERR_UNSUPPORTED;
+    if (!a->out || !a->counters || !a->pair_out || !a->pair_w || a->expected_arrivals != a->k_total)
+      return MOE_ERR_INVALID_ARG;
     if (a->out_dtype != MOE_F32 && a->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_INVALID_ARG;
@@ -438,7 +455,8 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   int32_t* nblk = reinterpret_cast<int32_t*>(ws + pl.off_nblk);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + pl.off_bexp);
-  float* acc = reinterpret_cast<float*>(ws + pl.off_acc);
+  float* acc = aux ? reinterpret_cast<float*>(ws + pl.off_acc) : nullptr;
+  float* pair = reinterpret_cast<float*>(ws + pl.off_pair);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
 
   hipEvent_t* tev = a->timing_events;
@@ -486,6 +504,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.x = static_cast<const uint8_t*>(x_stage);
   g.x_s = xs_stage;
   g.acc = acc;
+  g.pair_out = pair;
   g.out = a->out;
   g.out_bf16 = a->out_dtype == MOE_BF16;
 
@@ -523,6 +542,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   sp.counts = counts;
   sp.offsets = offsets;
   sp.num_blocks = nblk;
+  sp.chunk_base = sort_scratch_bytes(sp.P, pl.E_total) ? reinterpret_cast<int32_t*>(ws + pl.off_sortws) : nullptr;
   sp.zero_ptr = reinterpret_cast<uint4*>(ws + pl.zero_begin);
   sp.zero_vec = (long long)((pl.zero_end - pl.zero_begin) / 16);
   HIP_TRY(launch_sort(sp, main_s));

@@ -161,6 +161,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __shared__ uint32_t s_asc[2][BM];
   __shared__ uint32_t s_bsc[2][BROWS];
   __shared__ int s_tok[BM];
+  __shared__ int s_pair[BM];
   __shared__ float s_rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
   __shared__ float s_rw[BM];   // stage 2: pair weight / gate
   __shared__ float s_inv[BM];  // stage 2 A8W8: 448 / amax
@@ -191,19 +192,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int P = p.T * p.k_total;
   if (tid < BM) {
     const int slot = b * BM + tid;
-    int tok = -1;
+    int tok = -1, pair = -1;
     float rw = 0.f;
     if (p.dense) {
       tok = slot < p.T ? slot : -1;
       rw = (tok >= 0 && p.gamma) ? p.gamma[tok] : 1.0f;
     } else {
-      const int pair = p.sorted[slot];
+      pair = p.sorted[slot];
       if (pair < P) {
         tok = pair / p.k_total;
         if (STAGE == 2) rw = p.pair_w[pair];
+      } else {
+        pair = -1;
       }
     }
     s_tok[tid] = tok;
+    s_pair[tid] = pair;
     s_rw[tid] = rw;
     float rs = 1.0f, inv = 0.f;
     if (FMT == FMT_A8W8) {
@@ -504,23 +508,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       }
     }
   } else {
-    // ---- stage 2: store (dense addend) or weighted scatter-add + finalize ----
-    for (int r = wv; r < BM; r += 4) {
-      const int tok = s_tok[r];
-      if (tok < 0) continue;
-      const float wgt = s_rw[r];
-      float* dst = p.acc + (size_t)tok * p.H + n0;
-      for (int c = lane; c < BN; c += kWave) {
-        const float o = wgt * sT[r * LDT + c];
-        if (p.mode == 0) dst[c] = o;
-        else unsafeAtomicAdd(dst + c, o);
+    // ---- stage 2: STORE (dense addend) or per-pair rows + last-arrival sum ----
+    if (p.mode == 0) {
+      for (int r = wv; r < BM; r += 4) {
+        const int tok = s_tok[r];
+        if (tok < 0) continue;
+        const float wgt = s_rw[r];
+        float* dst = p.acc + (size_t)tok * p.H + n0;
+        for (int c = lane; c < BN; c += kWave) dst[c] = wgt * sT[r * LDT + c];
       }
-    }
-    if (p.mode == 1) {
-      // The accumulator is only touched by device-scope atomics, which are
-      // coherent across XCDs by themselves; the counter increment only has to
-      // wait until this wave's adds are acknowledged.  An agent-scope fence
-      // would also write back and invalidate the whole L2 of the XCD.
+    } else {
+      // Each (token, slot) pair owns one row of the pair buffer; rows are
+      // written with device-coherent stores so that whichever workgroup
+      // completes a (token, column tile) last can read them from any XCD.
+      for (int r = wv; r < BM; r += 4) {
+        const int pair = s_pair[r];
+        if (pair < 0) continue;
+        const float wgt = s_rw[r];
+        float* dst = p.pair_out + (size_t)pair * p.H + n0;
+        for (int c = lane; c < BN; c += kWave)
+          __hip_atomic_store(dst + c, wgt * sT[r * LDT + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // The counter increment only has to wait until this workgroup's row
+      // stores are acknowledged (they are coherent by themselves); an
+      // agent-scope fence would also write back and invalidate the XCD's L2.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -535,12 +546,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       }
       __syncthreads();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // last arrival: addend + the token's rows in slot order, one rounding
       for (int r = wv; r < BM; r += 4) {
         if (!s_done[r]) continue;
         const int tok = s_tok[r];
-        const float* src = p.acc + (size_t)tok * p.H + n0;
+        const float* rows = p.pair_out + (size_t)tok * p.k_total * p.H + n0;
         for (int c = lane; c < BN; c += kWave) {
-          const float v = __hip_atomic_load(src + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          float v = p.acc ? p.acc[(size_t)tok * p.H + n0 + c] : 0.0f;
+          for (int j = 0; j < p.k_total; ++j)
+            v += __hip_atomic_load(rows + (size_t)j * p.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (p.out_bf16)
             static_cast<uint16_t*>(p.out)[(size_t)tok * p.H + n0 + c] = (uint16_t)f32_to_bf16(v);
           else

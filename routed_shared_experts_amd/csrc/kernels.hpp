@@ -38,6 +38,7 @@ struct SortParams {
   int32_t* counts;
   int32_t* offsets;
   int32_t* num_blocks;
+  int32_t* chunk_base;  // [ceil(P/1024)][n_experts] scratch, or NULL (single-workgroup sort)
   uint4* zero_ptr;
   long long zero_vec;  // number of 16-byte vectors to clear
 };
@@ -63,7 +64,8 @@ struct GemmParams {
   int ld_h;
   const float* pair_w;
   const float* gamma;
-  float* acc;
+  float* acc;       // STORE: destination of gamma * S(x); ACCUMULATE: addend (or NULL)
+  float* pair_out;  // ACCUMULATE: [T * k_total][H] per-pair weighted outputs
   void* out;
   int out_bf16;
   int mode;  // 0 store, 1 accumulate
@@ -75,6 +77,7 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_gate_dot(const void* x, int x_f32, const void* g, int T, int H, int apply_sigmoid,
                            float* out, hipStream_t s);
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
+size_t sort_scratch_bytes(int P, int n_experts);
 hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s);
 
 }  // namespace moe

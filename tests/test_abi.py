@@ -169,8 +169,13 @@ def test_step_entry_points_reject_bad_arguments():
     assert L.moe_quant_mx(ctypes.c_void_p(0x1000), 2, 48, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000),
                           None) == m.MOE_ERR_INVALID_ARG  # H % 32
     p = ctypes.c_void_p(0x1000)
-    assert L.moe_sort_tokens(p, 4, 2, 8, 16, 16, p, p, p, p, p, None, 0, None) == m.MOE_ERR_INVALID_ARG  # capacity
-    assert L.moe_sort_tokens(p, 4, 2, 600, 16, 4096, p, p, p, p, p, None, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_sort_tokens(p, 4, 2, 8, 16, 16, p, p, p, p, p, None, 0, None, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_sort_tokens(p, 4, 2, 600, 16, 4096, p, p, p, p, p, None, 0, None, 0, None) == m.MOE_ERR_INVALID_ARG
+    big = m.moe_sort_scratch_bytes(8192, 9, 257)
+    assert big == 72 * 257 * 4 and m.moe_sort_scratch_bytes(32, 9, 65) == 0
+    cap = m.moe_sort_capacity(8192, 9, 257, 128)
+    assert L.moe_sort_tokens(p, 8192, 9, 257, 128, cap, p, p, p, p, p, p, big - 4, None, 0,
+                             None) == m.MOE_ERR_WORKSPACE
     sa = m.MoeStageArgs()
     assert L.moe_stage1(ctypes.byref(sa), None) == m.MOE_ERR_INVALID_ARG
     assert L.moe_stage2_accum(None, None) == m.MOE_ERR_INVALID_ARG

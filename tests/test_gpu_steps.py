@@ -110,24 +110,28 @@ def test_route_grouped_with_ties_and_k_equals_e(gpu):
     assert np.array_equal(ids, rid) and np.abs(w - rw).max() <= 1e-6
 
 
-def _sort_gpu(ids_np, n_experts, block_m, dev, zero=None):
+def _sort_gpu(ids_np, n_experts, block_m, dev, zero=None, scratch=True):
     m = _m()
     T, k = ids_np.shape
     cap = m.moe_sort_capacity(T, k, n_experts, block_m)
+    sb = m.moe_sort_scratch_bytes(T, k, n_experts)
+    scr = torch.empty(max(sb, 4), dtype=torch.uint8, device=dev) if (scratch and sb) else None
     ids = torch.from_numpy(ids_np.astype(np.int32)).to(dev)
     srt = torch.full((cap,), -7, dtype=torch.int32, device=dev)
     bexp = torch.full((cap // block_m,), -7, dtype=torch.int32, device=dev)
     counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
     offs = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
     nb = torch.empty(1, dtype=torch.int32, device=dev)
-    m.moe_sort_tokens(ids, n_experts, block_m, cap, srt, bexp, counts, offs, nb, zero=zero)
+    m.moe_sort_tokens(ids, n_experts, block_m, cap, srt, bexp, counts, offs, nb, scratch=scr, zero=zero)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in (srt, bexp, counts, offs, nb)]
 
 
+@pytest.mark.parametrize("scratch", [True, False])
 @pytest.mark.parametrize("block_m", [16, 32, 64, 128])
-@pytest.mark.parametrize("shape", [(1, 1, 1), (5, 2, 8), (32, 9, 65), (4096, 12, 68), (8192, 9, 257)])
-def test_sort_bit_exact(gpu, block_m, shape):
+@pytest.mark.parametrize("shape", [(1, 1, 1), (5, 2, 8), (32, 9, 65), (4096, 12, 68), (8192, 9, 257),
+                                   (1000, 9, 130)])
+def test_sort_bit_exact(gpu, block_m, shape, scratch):
     T, k, E = shape
     rng = np.random.default_rng(T * 31 + k)
     # distinct experts per token with a skewed (Zipf-like) load and some empty experts
@@ -136,7 +140,7 @@ def test_sort_bit_exact(gpu, block_m, shape):
     p /= p.sum()
     ids = np.stack([rng.choice(E, size=k, replace=False, p=p) if k <= (p > 0).sum() else rng.permutation(E)[:k]
                     for _ in range(T)])
-    srt, bexp, counts, offs, nb = _sort_gpu(ids, E, block_m, gpu)
+    srt, bexp, counts, offs, nb = _sort_gpu(ids, E, block_m, gpu, scratch=scratch)
     r = oracle.sort_tokens(ids, E, block_m)
     n = r["offsets"][-1]
     assert nb[0] == r["num_blocks"]
