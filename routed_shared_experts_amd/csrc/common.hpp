@@ -105,6 +105,42 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ---- wave64 reductions through DPP (no LDS round trips) ----------------------
+// row_shr:1,2,4,8 leave each row's total in its lane 15; row_bcast:15 and
+// row_bcast:31 carry rows 0-2 into row 3, so lane 63 ends with the wave total,
+// which readlane makes uniform.  Lanes with no DPP source keep their own value
+// (max) or add zero (sum).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xF>(v, v));
+  v = max(v, dpp_u32<0x112, 0xF>(v, v));
+  v = max(v, dpp_u32<0x114, 0xF>(v, v));
+  v = max(v, dpp_u32<0x118, 0xF>(v, v));
+  v = max(v, dpp_u32<0x142, 0xA>(v, v));
+  v = max(v, dpp_u32<0x143, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float dpp_wave_sum(float v) {
+  v += __uint_as_float(dpp_u32<0x111, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x112, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x114, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x118, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x142, 0xA>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x143, 0xC>(0u, __float_as_uint(v)));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+// Maximum of 64-bit keys (hi, lo) over the wave: the largest hi, then the
+// largest lo among the lanes holding it.  Returns the key, uniform.
+__device__ __forceinline__ uint64_t dpp_wave_max_key(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  const uint32_t mh = dpp_wave_max_u32(hi);
+  const uint32_t ml = dpp_wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
+}
+
 // Make this wave's LDS writes visible to its other lanes before they read.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");

@@ -25,119 +25,9 @@
 // (bytes 0-15 = K 16g.., bytes 16-31 = K 64+16g..) and the 32-element MX
 // blocks, and for the other formats it is a consistent permutation of K on
 // both operands.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
-
-template <int FMT>
-struct FmtInfo;
-template <>
-struct FmtInfo<FMT_F32> { static constexpr int esz = 4; static constexpr bool fp8 = false; };
-template <>
-struct FmtInfo<FMT_BF16> { static constexpr int esz = 2; static constexpr bool fp8 = false; };
-template <>
-struct FmtInfo<FMT_MX> { static constexpr int esz = 1; static constexpr bool fp8 = true; };
-template <>
-struct FmtInfo<FMT_A8W8> { static constexpr int esz = 1; static constexpr bool fp8 = true; };
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-template <int FMT>
-__device__ __forceinline__ void mfma_tile(f32x4& acc, const uint4& a0, const uint4& a1, const uint4& b0,
-                                          const uint4& b1, int sa, int sb) {
-  if constexpr (FMT == FMT_F32) {
-    const float* fa0 = reinterpret_cast<const float*>(&a0);
-    const float* fa1 = reinterpret_cast<const float*>(&a1);
-    const float* fb0 = reinterpret_cast<const float*>(&b0);
-    const float* fb1 = reinterpret_cast<const float*>(&b1);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa0[v], fb0[v], acc, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa1[v], fb1[v], acc, 0, 0, 0);
-  } else if constexpr (FMT == FMT_BF16) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b0),
-                                                  acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1),
-                                                  acc, 0, 0, 0);
-  } else {
-    i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    i32x8 B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, sa, 0, sb);
-  }
-}
-
-// Per-block problem description resolved from the expert index.
-struct ExpertView {
-  const uint8_t* wa;   // stage 1: gate rows; stage 2: W2 rows
-  const uint8_t* wb;   // stage 1: up rows
-  const uint8_t* sa;   // MX scales of wa rows
-  const uint8_t* sb;   // MX scales of wb rows
-  int ldw;             // weight row stride (elements)
-  int ldsc;            // MX scale row stride (bytes)
-  int width;           // stage 1: valid h columns; stage 2: valid K (h columns)
-  float wscale;        // A8W8 per-expert scale
-};
-
-template <int FMT, int STAGE>
-__device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e) {
-  constexpr int esz = FmtInfo<FMT>::esz;
-  ExpertView v{};
-  v.wscale = 1.0f;
-  const int H = p.H, I = p.I, Is = p.I_s;
-  if (e >= 0 && e < p.E) {
-    if (STAGE == 1) {
-      v.wa = p.w13 + (size_t)e * 2 * I * H * esz;
-      v.wb = v.wa + (size_t)I * H * esz;
-      v.ldw = H;
-      v.width = I;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.w13_s) + (size_t)e * 2 * I * (H / 32);
-        v.sb = v.sa + (size_t)I * (H / 32);
-        v.ldsc = H / 32;
-      }
-      if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w13_s)[e];
-    } else {
-      v.wa = p.w2 + (size_t)e * H * I * esz;
-      v.ldw = I;
-      v.width = I;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
-        v.ldsc = I / 32;
-      }
-      if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w2_s)[e];
-    }
-  } else {
-    // shared expert: whole (e < 0, dense) or pseudo-expert chunk c = e - E
-    const int c = (e < 0) ? 0 : e - p.E;
-    const int col0 = (e < 0) ? 0 : c * I;
-    const int w = (e < 0) ? Is : min(I, Is - col0);
-    if (STAGE == 1) {
-      v.wa = p.ws13 + (size_t)col0 * H * esz;
-      v.wb = p.ws13 + (size_t)(Is + col0) * H * esz;
-      v.ldw = H;
-      v.width = w;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.ws13_s) + (size_t)col0 * (H / 32);
-        v.sb = static_cast<const uint8_t*>(p.ws13_s) + (size_t)(Is + col0) * (H / 32);
-        v.ldsc = H / 32;
-      }
-      if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws13_s)[0];
-    } else {
-      v.wa = p.ws2 + (size_t)col0 * esz;
-      v.ldw = Is;
-      v.width = w;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.ws2_s) + col0 / 32;
-        v.ldsc = Is / 32;
-      }
-      if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws2_s)[0];
-    }
-  }
-  return v;
-}
 
 template <int FMT, int STAGE, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
@@ -189,41 +79,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const ExpertView ev = resolve_expert<FMT, STAGE>(p, e);
   if (STAGE == 1 && n0 >= ev.width) return;  // tile past a narrow pseudo-expert chunk
 
-  const int P = p.T * p.k_total;
-  if (tid < BM) {
-    const int slot = b * BM + tid;
-    int tok = -1, pair = -1;
-    float rw = 0.f;
-    if (p.dense) {
-      tok = slot < p.T ? slot : -1;
-      rw = (tok >= 0 && p.gamma) ? p.gamma[tok] : 1.0f;
-    } else {
-      pair = p.sorted[slot];
-      if (pair < P) {
-        tok = pair / p.k_total;
-        if (STAGE == 2) rw = p.pair_w[pair];
-      } else {
-        pair = -1;
-      }
-    }
-    s_tok[tid] = tok;
-    s_pair[tid] = pair;
-    s_rw[tid] = rw;
-    float rs = 1.0f, inv = 0.f;
-    if (FMT == FMT_A8W8) {
-      if (STAGE == 1) {
-        rs = tok >= 0 ? static_cast<const float*>(p.x_s)[tok] : 0.f;
-      } else {
-        const float amax = static_cast<const float*>(p.h_s)[slot];
-        if (amax > 0.f) {
-          inv = __fdiv_rn(448.0f, amax);
-          rs = __fdiv_rn(amax, 448.0f);
-        }
-      }
-    }
-    s_rs[tid] = rs;
-    s_inv[tid] = inv;
-  }
+  setup_rows<FMT, STAGE, BM>(p, b, tid, s_tok, s_pair, s_rw, s_rs, s_inv);
   __syncthreads();
 
   // ---- per-thread load descriptors ----
@@ -444,124 +300,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __syncthreads();
 
   if constexpr (STAGE == 1) {
-    const int ncol_valid = ev.width - n0;  // > 0
-    if constexpr (FMT == FMT_F32 || FMT == FMT_BF16 || FMT == FMT_A8W8) {
-      constexpr int VPC = (FMT == FMT_F32) ? 4 : 8;  // values per 16-byte chunk
-      constexpr int CPR = BN / VPC;                  // chunks per row
-      for (int cid = tid; cid < BM * CPR; cid += 256) {
-        const int r = cid / CPR, cc = cid % CPR;
-        const int c = cc * VPC;
-        const bool ok = s_tok[r] >= 0 && c < ncol_valid;
-        const size_t slot = (size_t)b * BM + r;
-        float amax = 0.f;
-        if (ok) {
-          const float* src = sT + r * LDT + c;
-          if constexpr (FMT == FMT_F32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.h) + slot * p.ld_h + n0 + c) =
-                make_float4(src[0], src[1], src[2], src[3]);
-          } else {
-            uint32_t wds[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t lo = f32_to_bf16(src[2 * u]), hi = f32_to_bf16(src[2 * u + 1]);
-              wds[u] = lo | (hi << 16);
-              amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(lo)), fabsf(bf16_to_f32(hi))));
-            }
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.h) + slot * p.ld_h + n0 + c) =
-                make_uint4(wds[0], wds[1], wds[2], wds[3]);
-          }
-        }
-        if constexpr (FMT == FMT_A8W8) {
-          // row amax of the bf16-rounded values: reduce over the CPR lanes of a row
-#pragma unroll
-          for (int o = 1; o < CPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-          if (cc == 0 && s_tok[r] >= 0)
-            atomicMax(reinterpret_cast<unsigned int*>(p.h_s) + slot, __float_as_uint(amax));
-        }
-      }
-    } else {  // MX: one thread per (row, 32-column block)
-      constexpr int BPR = BN / 32;
-      for (int task = tid; task < BM * BPR; task += 256) {
-        const int r = task / BPR, blk = task % BPR;
-        const int c = blk * 32;
-        if (s_tok[r] < 0 || c >= ncol_valid) continue;
-        const float* src = sT + r * LDT + c;
-        float v[32];
-        float amax = 0.f;
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          v[u] = bf16_to_f32(f32_to_bf16(src[u]));
-          amax = fmaxf(amax, fabsf(v[u]));
-        }
-        const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-        int X = (eb == 0) ? -127 : (eb - 127 - 8);
-        X = X < -127 ? -127 : (X > 127 ? 127 : X);
-        const float mul = __builtin_ldexpf(1.0f, -X);
-        uint32_t wds[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) wds[u] = pack4_e4m3(v[4 * u] * mul, v[4 * u + 1] * mul, v[4 * u + 2] * mul, v[4 * u + 3] * mul);
-        const size_t slot = (size_t)b * BM + r;
-        uint8_t* dst = p.h + slot * p.ld_h + n0 + c;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(wds[4], wds[5], wds[6], wds[7]);
-        static_cast<uint8_t*>(p.h_s)[slot * (p.ld_h / 32) + (n0 + c) / 32] = (uint8_t)(X + 127);
-      }
-    }
+    epilogue_stage1<FMT, BM, BN>(p, sT, LDT, b, n0, ev.width - n0, s_tok, tid);
   } else {
-    // ---- stage 2: STORE (dense addend) or per-pair rows + last-arrival sum ----
-    if (p.mode == 0) {
-      for (int r = wv; r < BM; r += 4) {
-        const int tok = s_tok[r];
-        if (tok < 0) continue;
-        const float wgt = s_rw[r];
-        float* dst = p.acc + (size_t)tok * p.H + n0;
-        for (int c = lane; c < BN; c += kWave) dst[c] = wgt * sT[r * LDT + c];
-      }
-    } else {
-      // Each (token, slot) pair owns one row of the pair buffer; rows are
-      // written with device-coherent stores so that whichever workgroup
-      // completes a (token, column tile) last can read them from any XCD.
-      for (int r = wv; r < BM; r += 4) {
-        const int pair = s_pair[r];
-        if (pair < 0) continue;
-        const float wgt = s_rw[r];
-        float* dst = p.pair_out + (size_t)pair * p.H + n0;
-        for (int c = lane; c < BN; c += kWave)
-          __hip_atomic_store(dst + c, wgt * sT[r * LDT + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // The counter increment only has to wait until this workgroup's row
-      // stores are acknowledged (they are coherent by themselves); an
-      // agent-scope fence would also write back and invalidate the XCD's L2.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid < BM) {
-        int done = 0;
-        const int tok = s_tok[tid];
-        if (tok >= 0) {
-          const int old = atomicAdd(p.counters + (size_t)tok * n_tiles + nt, 1);
-          done = (old == p.expected - 1);
-        }
-        s_done[tid] = done;
-      }
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // last arrival: addend + the token's rows in slot order, one rounding
-      for (int r = wv; r < BM; r += 4) {
-        if (!s_done[r]) continue;
-        const int tok = s_tok[r];
-        const float* rows = p.pair_out + (size_t)tok * p.k_total * p.H + n0;
-        for (int c = lane; c < BN; c += kWave) {
-          float v = p.acc ? p.acc[(size_t)tok * p.H + n0 + c] : 0.0f;
-          for (int j = 0; j < p.k_total; ++j)
-            v += __hip_atomic_load(rows + (size_t)j * p.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (p.out_bf16)
-            static_cast<uint16_t*>(p.out)[(size_t)tok * p.H + n0 + c] = (uint16_t)f32_to_bf16(v);
-          else
-            static_cast<float*>(p.out)[(size_t)tok * p.H + n0 + c] = v;
-        }
-      }
-    }
+    epilogue_stage2<BM, BN>(p, sT, LDT, n0, nt, n_tiles, s_tok, s_pair, s_rw, s_done, tid);
   }
 }
 
@@ -599,6 +340,9 @@ static hipError_t launch_stage(const GemmParams& p, int fmt, int bn, hipStream_t
 }
 
 hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s) {
+  // 16-row blocks: weights and activations streamed straight into registers,
+  // one wave per 32 (stage 1) or 64 (stage 2) columns of a block
+  if (p.block_m == 16 && wave_kernel_fits(p, stage, fmt)) return launch_gemm_wave(p, stage, fmt, s);
   return stage == 1 ? launch_stage<1>(p, fmt, bn, s) : launch_stage<2>(p, fmt, bn, s);
 }
 

@@ -1,0 +1,382 @@
+// Grouped GEMM for 16-row sorted blocks, one wave per workgroup (gfx950).
+//
+// Decode-sized batches (a few tokens per expert) make both stages stream the
+// expert weights once and do almost no arithmetic per byte (vLLM PR 65207's
+// decode profile is this regime).  A workgroup here is a single wave that owns
+// NCG consecutive 16-column groups of one block (stage 1: 2 groups = 32 h
+// columns, enough for one MX-32 block; stage 2: 4 groups = one 64-column
+// output tile).  Per group, stage 1 streams the 16 gate rows and the 16
+// matching up rows (SiLU-mul stays in registers) and stage 2 streams 16 rows
+// of W2; the prefetch runs on across group boundaries.  The weight rows are the MFMA M dimension and the block's (at most 16)
+// tokens the N dimension.  Weights go from HBM straight into MFMA operand
+// registers, D K-tiles ahead; the activation rows come from L2 through a
+// buffer descriptor (a padding row reads past the end of the buffer, i.e.
+// zeros, with no branch and no fetch).  There is no LDS and no barrier: the
+// many small independent workgroups hide each other's start-up latency.
+//
+// Stage 2 keeps the deterministic pair-row reduction: each wave stores the 64
+// columns of its weighted pair rows, then counts one arrival per token on the
+// (token, 64-column tile) counter; the last of the k_total arrivals sums the
+// addend and the token's rows in slot order and rounds once into out.
+//
+// K order as in the other GEMM kernels: lane group g feeds chunks g and 4+g of
+// each 128-byte K tile (the gfx950 16x16x128 f8f6f4 operand order); MX scales
+// come from lane r + 16b for K block b.
+#include "gemm_common.hpp"
+
+namespace moe {
+
+constexpr uint32_t kWvOutOfRange = 0x80000000u;  // buffer offset that reads as zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wv_rsrc(const void* base, uint32_t bytes) {
+  // raw (untyped) buffer, dword 3 = 0x00020000 on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 wv_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+template <int FMT, int STAGE, int D>
+__global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
+  constexpr int esz = FmtInfo<FMT>::esz;
+  constexpr int BM = 16;
+  constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);
+  constexpr int NW = (STAGE == 1) ? 2 : 1;    // weight rows per lane and group: gate + up, or W2
+  constexpr int NX = kQuantA ? 4 : 2;         // 16-byte activation loads per K tile
+  constexpr int NCG = (STAGE == 1) ? 2 : 4;   // 16-column groups per wave
+  constexpr int CW = 16 * NCG;                // columns per wave
+
+  const int lane = threadIdx.x;
+  const int g = lane / 16, l16 = lane % 16;
+  const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
+  const int ncw = width_max / CW;
+  const int b = blockIdx.x / ncw, c0 = (blockIdx.x % ncw) * CW;
+
+  // block expert and this lane's token, fetched together
+  const int slot_l = b * BM + l16;
+  int e, pair_l = -1, tok_l;
+  if (p.dense) {
+    if (b * BM >= p.T) return;
+    e = -1;
+    tok_l = slot_l < p.T ? slot_l : -1;
+  } else {
+    e = p.block_expert[b];  // -1 past the last block
+    const int pr = p.sorted[slot_l];
+    if (e < 0) return;
+    pair_l = pr < p.T * p.k_total ? pr : -1;
+    tok_l = pair_l >= 0 ? pair_l / p.k_total : -1;
+  }
+  const ExpertView ev = resolve_expert<FMT, STAGE>(p, e);
+  if (STAGE == 1 && c0 >= ev.width) return;
+  const int kbytes = (STAGE == 1) ? p.H * esz : ev.width * esz;  // a multiple of 128
+  const int nk = kbytes / 128;                                    // a multiple of D (launch)
+  const int ntiles = NCG * nk;
+
+  // ---- weights: lane row r = l16 of each group (clamped; rows past a narrow
+  // chunk are never stored) ----
+  const uint8_t* wbase[NW];
+  const uint8_t* sbase[NW];
+  wbase[0] = ev.wa + g * 16;
+  sbase[0] = ev.sa + g;
+  if constexpr (NW == 2) {
+    wbase[1] = ev.wb + g * 16;
+    sbase[1] = ev.sb + g;
+  }
+  // ---- activations: this lane's token row through a buffer descriptor ----
+  const bool xok = tok_l >= 0;
+  __amdgpu_buffer_rsrc_t xr, xsr;
+  uint32_t xoff, xsoff = 0;
+  if constexpr (STAGE == 1) {
+    xr = wv_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * esz));
+    xoff = xok ? (uint32_t)((size_t)tok_l * p.H * esz) + g * 16 : kWvOutOfRange;
+    if constexpr (FMT == FMT_MX) {
+      xsr = wv_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
+      xsoff = xok ? (uint32_t)(tok_l * (p.H / 32)) + g : kWvOutOfRange;
+    }
+  } else {
+    const size_t rows = (size_t)p.max_blocks * BM;
+    xr = wv_rsrc(p.h, (uint32_t)(rows * p.ld_h * (kQuantA ? 2 : esz)));
+    xoff = xok ? (uint32_t)((size_t)slot_l * p.ld_h * (kQuantA ? 2 : esz)) + g * 16 * (kQuantA ? 2 : 1)
+               : kWvOutOfRange;
+    if constexpr (FMT == FMT_MX) {
+      xsr = wv_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
+      xsoff = xok ? (uint32_t)(slot_l * (p.ld_h / 32)) + g : kWvOutOfRange;
+    }
+  }
+  float xinv = 0.f, rs = 1.0f;  // A8W8: stage-2 row quantisation (448 / amax) and row scale
+  if constexpr (FMT == FMT_A8W8) {
+    if (STAGE == 1) {
+      rs = xok ? static_cast<const float*>(p.x_s)[tok_l] : 0.f;
+    } else {
+      const float amax = xok ? static_cast<const float*>(p.h_s)[slot_l] : 0.f;
+      if (amax > 0.f) {
+        xinv = __fdiv_rn(448.0f, amax);
+        rs = __fdiv_rn(amax, 448.0f);
+      }
+    }
+  }
+
+  uint4 wb[D][NW][2];
+  int wsc[D][NW];
+  uint4 xb[D][NX];
+  int xsc[D];
+  // tile t = group * nk + k_tile; every load is unconditional (t clamped) so
+  // that no branch forces a wait for all outstanding loads
+  auto load = [&](int d, int t) {
+    t = t < ntiles ? t : ntiles - 1;
+    const int cgi = t / nk, kt = t - cgi * nk;
+    const int wrow = c0 + cgi * 16 + l16;
+    const int row = (STAGE == 1 && wrow >= ev.width) ? 0 : wrow;
+    const size_t off = (size_t)row * ev.ldw * esz + (size_t)kt * 128;
+#pragma unroll
+    for (int m = 0; m < NW; ++m) {
+      wb[d][m][0] = ld16(wbase[m] + off);
+      wb[d][m][1] = ld16(wbase[m] + off + 64);
+      if constexpr (FMT == FMT_MX) wsc[d][m] = sbase[m][(size_t)row * ev.ldsc + kt * 4];
+      else wsc[d][m] = 127;
+    }
+    if constexpr (kQuantA) {  // bf16 h: 32 bytes per 16-element chunk
+      const uint32_t o = xoff + (uint32_t)kt * 256;
+      xb[d][0] = wv_load16(xr, o);
+      xb[d][1] = wv_load16(xr, o + 16);
+      xb[d][2] = wv_load16(xr, o + 128);
+      xb[d][3] = wv_load16(xr, o + 144);
+    } else {
+      const uint32_t o = xoff + (uint32_t)kt * 128;
+      xb[d][0] = wv_load16(xr, o);
+      xb[d][1] = wv_load16(xr, o + 64);
+    }
+    if constexpr (FMT == FMT_MX)
+      xsc[d] = (int)__builtin_amdgcn_raw_buffer_load_b8(xsr, (int)(xsoff + (uint32_t)kt * 4), 0, 0);
+    else
+      xsc[d] = 127;
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, d);
+
+  f32x4 acc[NW];
+  auto compute = [&](int d) {
+    uint4 x0, x1;
+    if constexpr (kQuantA) {  // e4m3 with the row's 448 / amax on the fly
+      uint32_t o[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 lo = xb[d][2 * h], hi = xb[d][2 * h + 1];
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * h + u] = pack4_e4m3(bf16_to_f32(w[2 * u] & 0xFFFFu) * xinv, bf16_to_f32(w[2 * u] >> 16) * xinv,
+                                    bf16_to_f32(w[2 * u + 1] & 0xFFFFu) * xinv,
+                                    bf16_to_f32(w[2 * u + 1] >> 16) * xinv);
+      }
+      x0 = make_uint4(o[0], o[1], o[2], o[3]);
+      x1 = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      x0 = xb[d][0];
+      x1 = xb[d][1];
+    }
+#pragma unroll
+    for (int m = 0; m < NW; ++m) mfma_tile<FMT>(acc[m], wb[d][m][0], wb[d][m][1], x0, x1, wsc[d][m], xsc[d]);
+  };
+
+  // lane results: rows 4g..4g+3 of each group (columns c0 + 16 cgi + 4g + j),
+  // token l16
+  const float sc = rs * ev.wscale;
+  float res[NCG][4];
+#pragma unroll
+  for (int cgi = 0; cgi < NCG; ++cgi) {
+#pragma unroll
+    for (int m = 0; m < NW; ++m) acc[m] = f32x4{0, 0, 0, 0};
+    for (int kt0 = 0; kt0 < nk; kt0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        compute(d);
+        load(d, cgi * nk + kt0 + d + D);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      res[cgi][j] = (STAGE == 1) ? silu_mul(acc[0][j] * sc, acc[NW - 1][j] * sc) : acc[0][j] * sc;
+  }
+
+  if constexpr (STAGE == 1) {
+    const size_t slot = (size_t)slot_l;
+    if constexpr (FMT == FMT_MX) {
+      // one MX-32 block per token: the wave's 32 columns
+      float v[8], amax = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[q] = bf16_to_f32(f32_to_bf16(res[q / 4][q % 4]));
+        amax = fmaxf(amax, fabsf(v[q]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+      int X = (eb == 0) ? -127 : (eb - 127 - 8);
+      X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      const float mul = __builtin_ldexpf(1.0f, -X);
+      if (xok && c0 < ev.width) {
+        uint8_t* dst = p.h + slot * p.ld_h + c0 + 4 * g;
+        *reinterpret_cast<uint32_t*>(dst) = pack4_e4m3(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
+        *reinterpret_cast<uint32_t*>(dst + 16) = pack4_e4m3(v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul);
+        if (g == 0) static_cast<uint8_t*>(p.h_s)[slot * (p.ld_h / 32) + c0 / 32] = (uint8_t)(X + 127);
+      }
+    } else {
+      float amax = 0.f;
+#pragma unroll
+      for (int cgi = 0; cgi < NCG; ++cgi) {
+        const int col = c0 + cgi * 16 + 4 * g;
+        const bool ok = xok && col < ev.width;
+        if constexpr (FMT == FMT_F32) {
+          if (ok) *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.h) + slot * p.ld_h + col) =
+              make_float4(res[cgi][0], res[cgi][1], res[cgi][2], res[cgi][3]);
+        } else {
+          uint32_t bits[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bits[j] = f32_to_bf16(res[cgi][j]);
+            if (ok) amax = fmaxf(amax, fabsf(bf16_to_f32(bits[j])));
+          }
+          if (ok) *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.h) + slot * p.ld_h + col) =
+              make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+        }
+      }
+      if constexpr (FMT == FMT_A8W8) {
+        // row amax of the bf16-rounded values over the wave's columns
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        if (g == 0 && xok) atomicMax(reinterpret_cast<unsigned int*>(p.h_s) + slot, __float_as_uint(amax));
+      }
+    }
+  } else {
+    if (p.mode == 0) {  // STORE: the dense shared expert's gamma * S(x) as the addend
+      if (xok) {
+        const float gm = p.gamma ? p.gamma[tok_l] : 1.0f;
+#pragma unroll
+        for (int cgi = 0; cgi < NCG; ++cgi)
+          *reinterpret_cast<float4*>(p.acc + (size_t)tok_l * p.H + c0 + cgi * 16 + 4 * g) =
+              make_float4(gm * res[cgi][0], gm * res[cgi][1], gm * res[cgi][2], gm * res[cgi][3]);
+      }
+      return;
+    }
+    // ACCUMULATE: this pair's 64 columns with device-coherent stores
+    if (pair_l >= 0) {
+      const float wgt = p.pair_w[pair_l];
+      uint64_t* dst = reinterpret_cast<uint64_t*>(p.pair_out + (size_t)pair_l * p.H + c0 + 4 * g);
+#pragma unroll
+      for (int cgi = 0; cgi < NCG; ++cgi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint64_t v = (uint64_t)__float_as_uint(wgt * res[cgi][2 * h]) |
+                             ((uint64_t)__float_as_uint(wgt * res[cgi][2 * h + 1]) << 32);
+          __hip_atomic_store(dst + cgi * 8 + h, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // count the arrival once the stores are acknowledged (no agent-scope fence:
+    // on multi-XCD parts it would write back and invalidate the whole L2)
+    __builtin_amdgcn_s_waitcnt(0);
+    const int n_tiles = p.H / 64;
+    const int tile = c0 / 64;
+    int done = 0;
+    if (g == 0 && pair_l >= 0) {
+      const int old = atomicAdd(p.counters + (size_t)tok_l * n_tiles + tile, 1);
+      done = (old == p.expected - 1);
+    }
+    done = __shfl(done, l16, kWave);  // broadcast to the token's 4 lanes
+    if (done) {
+      // last arrival: addend + rows in slot order; this lane sums 16 columns
+      const int cbase = c0 + 16 * g;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = p.acc ? p.acc[(size_t)tok_l * p.H + cbase + q] : 0.0f;
+      const uint64_t* rows = reinterpret_cast<const uint64_t*>(p.pair_out + (size_t)tok_l * p.k_total * p.H + cbase);
+      for (int jj = 0; jj < p.k_total; ++jj) {
+        uint64_t t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          t[q] = __hip_atomic_load(rows + (size_t)jj * (p.H / 2) + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          v[2 * q] += __uint_as_float((uint32_t)t[q]);
+          v[2 * q + 1] += __uint_as_float((uint32_t)(t[q] >> 32));
+        }
+      }
+      if (p.out_bf16) {
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
+        uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok_l * p.H + cbase);
+        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      } else {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok_l * p.H + cbase);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    }
+  }
+}
+
+// Largest prefetch depth (4, 2 or 1) dividing the K-tile count of every
+// expert the launch can meet (routed width, shared width, last pseudo chunk).
+static int wave_depth(const GemmParams& p, int stage, int fmt) {
+  const int esz = fmt == FMT_F32 ? 4 : (fmt == FMT_BF16 ? 2 : 1);
+  int g = 0;
+  auto gcd = [](int a, int b) { while (b) { int t = a % b; a = b; b = t; } return a; };
+  if (stage == 1) {
+    g = p.H * esz / 128;
+  } else if (p.dense) {
+    g = p.I_s * esz / 128;
+  } else {
+    g = p.I * esz / 128;
+    if (p.n_pseudo > 0) g = gcd(g, (p.I_s - (p.n_pseudo - 1) * p.I) * esz / 128);
+  }
+  return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1);
+}
+
+template <int FMT, int STAGE>
+static hipError_t launch_wv(const GemmParams& p, int depth, hipStream_t s) {
+  constexpr int CW = (STAGE == 1) ? 32 : 64;
+  const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
+  const dim3 grid((unsigned)(p.max_blocks * (width_max / CW)));
+  switch (depth) {
+    case 4: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 4>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 2>), grid, dim3(64), 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 1>), grid, dim3(64), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+// Activation buffers are addressed with 32-bit buffer offsets; widths must
+// split into whole waves (32 columns in stage 1, 64 in stage 2).
+bool wave_kernel_fits(const GemmParams& p, int stage, int fmt) {
+  const size_t esz = fmt == FMT_F32 ? 4 : (fmt == FMT_BF16 ? 2 : 1);
+  const size_t hsz = fmt == FMT_A8W8 ? 2 : esz;
+  const size_t bytes = stage == 1 ? (size_t)p.T * p.H * esz : (size_t)p.max_blocks * 16 * p.ld_h * hsz;
+  if (bytes >= 0x7FFFFFFFu) return false;
+  if (stage == 1) return p.I % 32 == 0 && p.I_s % 32 == 0;
+  return p.H % 64 == 0;
+}
+
+hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t s) {
+  const int depth = wave_depth(p, stage, fmt);
+  if (stage == 1) {
+    switch (fmt) {
+      case FMT_F32: return launch_wv<FMT_F32, 1>(p, depth, s);
+      case FMT_BF16: return launch_wv<FMT_BF16, 1>(p, depth, s);
+      case FMT_MX: return launch_wv<FMT_MX, 1>(p, depth, s);
+      case FMT_A8W8: return launch_wv<FMT_A8W8, 1>(p, depth, s);
+    }
+  } else {
+    switch (fmt) {
+      case FMT_F32: return launch_wv<FMT_F32, 2>(p, depth, s);
+      case FMT_BF16: return launch_wv<FMT_BF16, 2>(p, depth, s);
+      case FMT_MX: return launch_wv<FMT_MX, 2>(p, depth, s);
+      case FMT_A8W8: return launch_wv<FMT_A8W8, 2>(p, depth, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -79,5 +79,7 @@ hipError_t launch_gate_dot(const void* x, int x_f32, const void* g, int T, int H
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 size_t sort_scratch_bytes(int P, int n_experts);
 hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s);
+hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t s);
+bool wave_kernel_fits(const GemmParams& p, int stage, int fmt);
 
 }  // namespace moe

@@ -8,7 +8,8 @@
 //    folded into the weights (vLLM PR 65207, "Purpose", commit 1), with
 //    deterministic tie-breaks (equal scores -> lower index).
 // Selection keys are (order-preserving score bits << 32 | ~index), so one
-// 64-bit wave max per round picks the winner and applies the tie rule.
+// 64-bit wave max per round (two DPP reductions) picks the winner and applies
+// the tie rule.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,7 +40,7 @@ __device__ void gate_dot_wave(const RouteParams& p, int t, int lane, float* gamm
       }
     }
   }
-  sum = wave_sum(sum);
+  sum = dpp_wave_sum(sum);
   *gamma_out_val = spec_sigmoid(sum);
 }
 
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_kernel(RouteParams p
     }
     kept = 0;
     for (int r = 0; r < p.topk_group; ++r) {
-      uint64_t m = wave_max_u64(gkey);
+      uint64_t m = dpp_wave_max_key(gkey);
       int g = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
       kept |= 1ull << g;
       if (lane == g) gkey = 0;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_kernel(RouteParams p
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) best = cand[i] > best ? cand[i] : best;
-    uint64_t m = wave_max_u64(best);
+    uint64_t m = dpp_wave_max_key(best);
     int e = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
     if ((e % kWave) == lane) {
 #pragma unroll
@@ -181,16 +182,16 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_kernel(RouteParams p
     float ex = (lane < p.topk) ? __expf(my_v - lmax) : 0.f;
     float denom;
     if (p.renorm) {
-      denom = wave_sum(ex);
+      denom = dpp_wave_sum(ex);
     } else {
       float part = 0.f;
       for (int e = lane; e < E; e += kWave) part += __expf(val[e] - lmax);
-      denom = wave_sum(part);
+      denom = dpp_wave_sum(part);
     }
     wgt = ex / denom;
   } else {
     float sg = (lane < p.topk) ? my_v : 0.f;
-    float denom = p.renorm ? wave_sum(sg) : 1.0f;
+    float denom = p.renorm ? dpp_wave_sum(sg) : 1.0f;
     wgt = sg / denom;
   }
   wgt *= p.scale;

@@ -27,16 +27,19 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("block_m", [0, 16])
 @pytest.mark.parametrize("mode", ["pseudo", "aux"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_layers_all_outputs(gpu, name, mode):
+def test_small_layers_all_outputs(gpu, name, mode, block_m):
+    """block_m = 16 takes the register-streamed (skinny) GEMM kernels, the
+    automatic choice takes the LDS-staged ones at these sizes."""
     cfg = SMALL[name]
     if mode == "pseudo" and cfg.fmt == "a8w8" and cfg.I_s > cfg.I:
         pytest.skip("per-row fp8 intermediate needs a single pseudo chunk")
     inp = inputs(cfg, gpu)
-    out, _ = run_forward(cfg, inp, mode)
+    out, _ = run_forward(cfg, inp, mode, block_m=block_m)
     rel, floor, _ = assert_close(cfg, out, inp)
-    print(f"{name}/{mode}: max|err|/rms={rel:.3e} floor={floor:.3e}")
+    print(f"{name}/{mode}/bm{block_m}: max|err|/rms={rel:.3e} floor={floor:.3e}")
 
 
 @pytest.mark.parametrize("block_m", [16, 32, 64, 128])
@@ -80,11 +83,12 @@ def test_prefill_bf16_workload_sampled(gpu, mode):
     print(f"prefill_bf16/{mode}: max|err|/rms={rel:.3e} floor={floor:.3e}")
 
 
+@pytest.mark.parametrize("block_m", [0, 16])
 @pytest.mark.parametrize("mode", ["pseudo", "aux"])
-def test_mxfp8_workload_sampled(gpu, mode):
+def test_mxfp8_workload_sampled(gpu, mode, block_m):
     cfg = workloads.CONFIGS["mxfp8"]
     inp = inputs(cfg, gpu)
-    out, _ = run_forward(cfg, inp, mode)
+    out, _ = run_forward(cfg, inp, mode, block_m=block_m)
     rel, floor, _ = assert_close(cfg, out, inp, tokens=_sample(cfg.T, 24, 2), lazy=True)
     print(f"mxfp8/{mode}: max|err|/rms={rel:.3e} floor={floor:.3e}")
 
