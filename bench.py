@@ -105,19 +105,15 @@ def main():
     inp = workloads.generate(cfg, device=dev)
     wbytes = workloads.bytes_per_weight(cfg.fmt) * 3.0 * cfg.H * (cfg.E * cfg.I + cfg.I_s)
     copies = args.copies or max(1, min(6, int(np.ceil(3 * 256e6 / wbytes))))
-    # rotate weight copies so the per-step footprint exceeds the 256 MB Infinity Cache
-    sets = [inp]
-    for _ in range(copies - 1):
-        c = dict(inp)
-        for k in ("w13", "w2", "ws13", "ws2", "w13_scale", "w2_scale", "ws13_scale", "ws2_scale"):
-            if inp.get(k) is not None:
-                c[k] = inp[k].clone()
-        sets.append(c)
+    # rotate weight copies so the per-step footprint exceeds the 256 MB Infinity
+    # Cache; each copy is a tiled (load-time packed) set of the same weights
+    packed_sets = [m.pack_weights(cfg, inp) for _ in range(copies)]
+    torch.cuda.synchronize()
 
     modes = ["pseudo", "aux"] if args.mode == "best" else [args.mode]
     results = {}
     for mode in modes:
-        layers = [m.MoeLayer(cfg, s, shared_mode=mode) for s in sets]
+        layers = [m.MoeLayer(cfg, inp, shared_mode=mode, packed=pk) for pk in packed_sets]
         out = layers[0].out
         for L in layers[1:]:
             L.args.out = m._ptr(out)

@@ -102,6 +102,24 @@ typedef enum {
   MOE_FEATURE_BF16 = 7
 } moe_feature;
 
+/* Weight layout.  Logically every weight matrix is row-major: rows = output
+ * features, row_bytes = K * element size (rows % 16 == 0, row_bytes % 128 ==
+ * 0).  The GEMM kernels read it in a tiled order instead, so that each 64-lane
+ * MFMA operand load is 1024 contiguous bytes: 16-row x 128-byte tiles of 2048
+ * contiguous bytes, row block major, K tile minor.  Inside a tile, byte b
+ * (0..15) of 16-byte chunk c (0..7) of tile row r (0..15) sits at
+ *     (c / 4) * 1024 + ((c % 4) * 16 + r) * 16 + b.
+ * MX32 scale matrices (rows x row_bytes / 32 bytes, one e8m0 byte per 32
+ * elements) are tiled alike: 16 rows x 4 scale bytes per 64-byte tile, scale
+ * q (0..3) of tile row r at q * 16 + r.  Matrices of consecutive experts stay
+ * consecutive (a tiled [n][rows][row_bytes] array is n tiled matrices back to
+ * back), and a 16-row-aligned row range stays a contiguous byte range.
+ * moe_pack_weights / moe_pack_mx_scales convert once, at load time. */
+typedef enum {
+  MOE_LAYOUT_ROW_MAJOR = 0, /* accepted only by the pack functions */
+  MOE_LAYOUT_TILED = 1      /* required by moe_forward, moe_stage1, moe_stage2_accum */
+} moe_layout;
+
 /* One family of expert weights (routed: n = E, width I; shared: n = 1, width I_s). */
 typedef struct {
   const void* w13;       /* [n][2*width][H] gate rows then up rows */
@@ -110,6 +128,7 @@ typedef struct {
   const void* w2_scale;  /* PER_EXPERT: float[n]; MX32: uint8 [n][H][width/32]; else NULL */
   int32_t dtype;         /* moe_dtype */
   int32_t scale;         /* moe_scale: NONE, PER_EXPERT or MX32 */
+  int32_t layout;        /* moe_layout of w13, w2 and MX32 scales: must be MOE_LAYOUT_TILED */
 } moe_weights;
 
 /* Everything one layer forward needs. */
@@ -222,6 +241,20 @@ int32_t moe_sort_capacity(int32_t T, int32_t k_total, int32_t n_experts, int32_t
  * with three launches instead of one workgroup (0 when it would not use it).
  * Host-only. */
 size_t moe_sort_scratch_bytes(int32_t T, int32_t k_total, int32_t n_experts);
+
+/* Converts a row-major weight matrix (or several stacked ones) to the tiled
+ * layout described at moe_layout.  src, dst: device, 16-byte aligned, not
+ * overlapping, rows * row_bytes bytes each; rows % 16 == 0, row_bytes % 128 ==
+ * 0.  The caller owns both buffers.  Asynchronous on stream. */
+moe_status moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes,
+                            hipStream_t stream);
+
+/* Converts a row-major MX32 scale matrix ([rows][scale_bytes] e8m0 bytes,
+ * scale_bytes = row_bytes / 32 of the matching weight matrix) to the tiled
+ * layout.  rows % 16 == 0, scale_bytes % 4 == 0; src, dst: device, 4-byte
+ * aligned, not overlapping.  Asynchronous on stream. */
+moe_status moe_pack_mx_scales(const void* src, void* dst, int64_t rows, int32_t scale_bytes,
+                              hipStream_t stream);
 
 /* Token-by-expert sort (vLLM PR 65207, commit 2 and the review's sorting
  * experiment).  For pair p = t*k_total + j with expert topk_ids[p]:

@@ -10,7 +10,8 @@ The entry points mirror the C ABI in ``include/moe.h``: ``moe_route``,
 ``shared_gate_dot``, ``moe_quant_mx``, ``moe_sort_tokens``, ``moe_stage1``,
 ``moe_stage2_accum`` and the fused ``moe_forward``, plus ``moe_validate``,
 ``moe_workspace_bytes``, ``moe_sort_capacity``, ``moe_query_feature`` and
-``moe_status_str``.
+``moe_status_str``; ``moe_pack_weights`` / ``moe_pack_mx_scales`` convert
+row-major weights to the tiled layout the GEMM kernels read.
 """
 
 import ctypes
@@ -26,6 +27,7 @@ MOE_SCALE_NONE, MOE_SCALE_PER_ROW, MOE_SCALE_PER_EXPERT, MOE_SCALE_MX32 = 0, 1, 
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_SHARED_NONE, MOE_SHARED_PSEUDO, MOE_SHARED_AUX, MOE_SHARED_AUTO = 0, 1, 2, 3
 MOE_STAGE2_STORE, MOE_STAGE2_ACCUMULATE = 0, 1
+MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_TILED = 0, 1
 (MOE_FEATURE_ACCUMULATE_OUTPUT, MOE_FEATURE_PSEUDO_SHARED, MOE_FEATURE_AUX_STREAM,
  MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16) = 1, 2, 3, 4, 5, 6, 7
 
@@ -34,15 +36,15 @@ SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE
 
 # Exported symbols, in the order of include/moe.h.
 EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_route", "shared_gate_dot",
-           "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_sort_tokens", "moe_stage1", "moe_stage2_accum",
-           "moe_query_feature", "moe_status_str"]
+           "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_pack_weights", "moe_pack_mx_scales",
+           "moe_sort_tokens", "moe_stage1", "moe_stage2_accum", "moe_query_feature", "moe_status_str"]
 
 c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w13", c_void_p), ("w2", c_void_p), ("w13_scale", c_void_p), ("w2_scale", c_void_p),
-                ("dtype", c_int32), ("scale", c_int32)]
+                ("dtype", c_int32), ("scale", c_int32), ("layout", c_int32)]
 
 
 class MoeForwardArgs(ctypes.Structure):
@@ -90,6 +92,8 @@ def _load():
         "moe_quant_mx": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "moe_sort_capacity": (c_int32, [c_int32, c_int32, c_int32, c_int32]),
         "moe_sort_scratch_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "moe_pack_weights": (c_int32, [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_void_p]),
+        "moe_pack_mx_scales": (c_int32, [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_void_p]),
         "moe_sort_tokens": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                       c_size_t, c_void_p]),
@@ -172,6 +176,28 @@ def moe_quant_mx(x, codes, scales, stream=None):
     _check(st, "moe_quant_mx")
 
 
+def moe_pack_weights(src, dst=None, stream=None):
+    """Tiled copy of a row-major weight tensor whose last dimension is K (any
+    leading dimensions: stacked matrices); returns dst (new if None)."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    row_bytes = src.shape[-1] * src.element_size()
+    rows = src.numel() * src.element_size() // row_bytes
+    _check(_lib.moe_pack_weights(_ptr(src), _ptr(dst), rows, row_bytes, _stream(stream)), "moe_pack_weights")
+    return dst
+
+
+def moe_pack_mx_scales(src, dst=None, stream=None):
+    """Tiled copy of a row-major uint8 MX32 scale tensor (last dimension =
+    scale bytes per row); returns dst (new if None)."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    sb = src.shape[-1]
+    _check(_lib.moe_pack_mx_scales(_ptr(src), _ptr(dst), src.numel() // sb, sb, _stream(stream)),
+           "moe_pack_mx_scales")
+    return dst
+
+
 def moe_sort_scratch_bytes(T, k_total, n_experts):
     return int(_lib.moe_sort_scratch_bytes(T, k_total, n_experts))
 
@@ -206,4 +232,4 @@ def moe_forward(args, workspace, main_stream=None, aux_stream=None, ev_fork=None
     _check(st, "moe_forward")
 
 
-from .layer import (FORMATS, weights_struct, forward_args, MoeLayer)  # noqa: E402,F401
+from .layer import (FORMATS, weights_struct, forward_args, pack_weights, MoeLayer)  # noqa: E402,F401

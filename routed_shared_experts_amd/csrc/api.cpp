@@ -40,6 +40,17 @@ bool weights_ok(const moe_weights& w, int fmt) {
   return true;
 }
 
+// MOE_OK, or the error for a weight family in a layout the kernels do not read
+moe_status layout_status(const moe_weights& w) {
+  if (w.layout == MOE_LAYOUT_TILED) return MOE_OK;
+  return w.layout == MOE_LAYOUT_ROW_MAJOR ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+}
+
+bool overlaps(const void* a, const void* b, size_t n) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + n && y < x + n;
+}
+
 int auto_block_m(double rows_per_expert) {
   if (rows_per_expert <= 16) return 16;
   if (rows_per_expert <= 48) return 32;
@@ -82,6 +93,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   const int fmt = weights_fmt(a->routed);
   if (fmt < 0) return MOE_ERR_UNSUPPORTED;
   if (!weights_ok(a->routed, fmt)) return MOE_ERR_INVALID_ARG;
+  if (const moe_status st = layout_status(a->routed)) return st;
   // activation format must match the weight format
   if (fmt == FMT_F32 && a->x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if ((fmt == FMT_BF16 || fmt == FMT_MX) && a->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -102,6 +114,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
     const int sfmt = weights_fmt(a->shared);
     if (sfmt < 0) return MOE_ERR_UNSUPPORTED;
     if (!weights_ok(a->shared, sfmt)) return MOE_ERR_INVALID_ARG;
+    if (const moe_status st = layout_status(a->shared)) return st;
     if (a->shared_mode == MOE_SHARED_PSEUDO) {
       // fusion only when the shared weights use the routed experts' format
       if (sfmt != fmt) return MOE_ERR_UNSUPPORTED;
@@ -303,6 +316,22 @@ moe_status shared_gate_dot(const void* x, int32_t x_dtype, const void* g, int32_
   return MOE_OK;
 }
 
+moe_status moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes, hipStream_t stream) {
+  if (!src || !dst || rows < 0 || row_bytes <= 0 || rows % 16 || row_bytes % 128) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (overlaps(src, dst, (size_t)rows * row_bytes)) return MOE_ERR_INVALID_ARG;
+  HIP_TRY(launch_pack_weights(src, dst, rows, row_bytes, stream));
+  return MOE_OK;
+}
+
+moe_status moe_pack_mx_scales(const void* src, void* dst, int64_t rows, int32_t scale_bytes, hipStream_t stream) {
+  if (!src || !dst || rows < 0 || scale_bytes <= 0 || rows % 16 || scale_bytes % 4) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u)) return MOE_ERR_INVALID_ARG;
+  if (overlaps(src, dst, (size_t)rows * scale_bytes)) return MOE_ERR_INVALID_ARG;
+  HIP_TRY(launch_pack_scales(src, dst, rows, scale_bytes, stream));
+  return MOE_OK;
+}
+
 moe_status moe_quant_mx(const void* x, int32_t T, int32_t H, uint8_t* codes, uint8_t* scales,
                         hipStream_t stream) {
   if (!x || !codes || !scales || T <= 0 || H <= 0 || H % 32 || !aligned16(x) || ((uintptr_t)codes & 7u))
@@ -364,6 +393,10 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   if (!weights_ok(wf, fmt)) return MOE_ERR_INVALID_ARG;
   if ((a->n_pseudo > 0 || a->dense) && (a->I_s <= 0 || weights_fmt(a->shared) != fmt || !weights_ok(a->shared, fmt)))
     return MOE_ERR_INVALID_ARG;
+  if (const moe_status st = layout_status(wf)) return st;
+  if (a->n_pseudo > 0 || a->dense) {
+    if (const moe_status st = layout_status(a->shared)) return st;
+  }
   if (!a->dense && (!a->sorted_pair_ids || !a->block_expert || !a->num_blocks)) return MOE_ERR_INVALID_ARG;
   if (a->dense && a->max_blocks * a->block_m < a->T) return MOE_ERR_INVALID_ARG;
   const int kt = ktile_elems(fmt);

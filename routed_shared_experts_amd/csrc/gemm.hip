@@ -114,15 +114,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     b_ok[q] = false;
     b_ptr[q] = nullptr;
     if (cid < B_CH) {
+      // chunk c of weight row col in K tile 0 of the tiled layout; a K tile
+      // further on is 2048 bytes later
       if (STAGE == 1) {
         const int col = n0 + (r % BN);
         b_ok[q] = col < ev.width;
+        const int cr = b_ok[q] ? col : 0;
         const uint8_t* base = (r < BN) ? ev.wa : ev.wb;
-        b_ptr[q] = base + ((size_t)(b_ok[q] ? col : 0) * ev.ldw * esz + c * 16);
+        b_ptr[q] = base + tile_off(ev, cr / 16, 0) + (c / 4) * 1024 + ((c % 4) * 16 + cr % 16) * 16;
       } else {
         const int col = n0 + r;  // output feature (row of W2)
         b_ok[q] = true;
-        b_ptr[q] = ev.wa + ((size_t)col * ev.ldw * esz + c * 16);
+        b_ptr[q] = ev.wa + tile_off(ev, col / 16, 0) + (c / 4) * 1024 + ((c % 4) * 16 + col % 16) * 16;
       }
     }
   }
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int q = 0; q < B_PER; ++q) {
       const int c = (tid + q * 256) % 8;
       const bool kin = (kb + c * 16) < kbytes;
-      rb[q] = (b_ok[q] && kin) ? ld16(b_ptr[q] + kb) : make_uint4(0, 0, 0, 0);
+      rb[q] = (b_ok[q] && kin) ? ld16(b_ptr[q] + (size_t)kt * 2048) : make_uint4(0, 0, 0, 0);
     }
     if constexpr (FMT == FMT_MX) {
       // 4 e8m0 bytes per row per K tile; blocks past the valid K read as 2^0
@@ -169,15 +172,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       }
       if (tid < BROWS) {
         uint32_t v = 0x7F7F7F7Fu;
+        // the 4 scale bytes of (row, K tile) sit 16 bytes apart in the tile
+        const uint8_t* sp = nullptr;
         if (STAGE == 1) {
           const int col = n0 + (tid % BN);
-          if (col < ev.width) {
-            const uint8_t* base = (tid < BN) ? ev.sa : ev.sb;
-            v = *reinterpret_cast<const uint32_t*>(base + (size_t)col * ev.ldsc + kblk0);
-          }
+          if (col < ev.width) sp = ((tid < BN) ? ev.sa : ev.sb) + scale_tile_off(ev, col / 16, kt) + col % 16;
         } else {
-          v = *reinterpret_cast<const uint32_t*>(ev.sa + (size_t)(n0 + tid) * ev.ldsc + kblk0);
+          const int col = n0 + tid;
+          sp = ev.sa + scale_tile_off(ev, col / 16, kt) + col % 16;
         }
+        if (sp) v = (uint32_t)sp[0] | ((uint32_t)sp[16] << 8) | ((uint32_t)sp[32] << 16) | ((uint32_t)sp[48] << 24);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (kblk0 + q >= kblk_valid) v = (v & ~(0xFFu << (8 * q))) | (0x7Fu << (8 * q));

@@ -49,17 +49,28 @@ __device__ __forceinline__ void mfma_tile(f32x4& acc, const uint4& a0, const uin
   }
 }
 
-// Per-block problem description resolved from the expert index.
+// Per-block problem description resolved from the expert index.  Weights
+// and MX scales are in the tiled layout (16-row x 128-byte tiles of 2048
+// bytes, row block major; 64-byte scale tiles), so a view is the base of its
+// row block 0 plus the tile count of a full matrix row and a first K tile.
 struct ExpertView {
   const uint8_t* wa;   // stage 1: gate rows; stage 2: W2 rows
   const uint8_t* wb;   // stage 1: up rows
   const uint8_t* sa;   // MX scales of wa rows
   const uint8_t* sb;   // MX scales of wb rows
-  int ldw;             // weight row stride (elements)
-  int ldsc;            // MX scale row stride (bytes)
+  int nkt;             // K tiles per row of the underlying matrix
+  int kt0;             // first K tile of this view (shared W2 pseudo-expert chunk)
   int width;           // stage 1: valid h columns; stage 2: valid K (h columns)
   float wscale;        // A8W8 per-expert scale
 };
+
+// Byte offset of tile (row block rb, K tile kt) of a view, and of its scales.
+__device__ __forceinline__ size_t tile_off(const ExpertView& v, int rb, int kt) {
+  return ((size_t)rb * v.nkt + v.kt0 + kt) * 2048;
+}
+__device__ __forceinline__ size_t scale_tile_off(const ExpertView& v, int rb, int kt) {
+  return ((size_t)rb * v.nkt + v.kt0 + kt) * 64;
+}
 
 template <int FMT, int STAGE>
 __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e) {
@@ -71,22 +82,18 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
     if (STAGE == 1) {
       v.wa = p.w13 + (size_t)e * 2 * I * H * esz;
       v.wb = v.wa + (size_t)I * H * esz;
-      v.ldw = H;
+      v.nkt = H * esz / 128;
       v.width = I;
       if (FMT == FMT_MX) {
         v.sa = static_cast<const uint8_t*>(p.w13_s) + (size_t)e * 2 * I * (H / 32);
         v.sb = v.sa + (size_t)I * (H / 32);
-        v.ldsc = H / 32;
       }
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w13_s)[e];
     } else {
       v.wa = p.w2 + (size_t)e * H * I * esz;
-      v.ldw = I;
+      v.nkt = I * esz / 128;
       v.width = I;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
-        v.ldsc = I / 32;
-      }
+      if (FMT == FMT_MX) v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w2_s)[e];
     }
   } else {
@@ -95,24 +102,23 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
     const int col0 = (e < 0) ? 0 : c * I;
     const int w = (e < 0) ? Is : min(I, Is - col0);
     if (STAGE == 1) {
+      // rows col0.. of the gate and up halves (col0 is a multiple of 16)
       v.wa = p.ws13 + (size_t)col0 * H * esz;
       v.wb = p.ws13 + (size_t)(Is + col0) * H * esz;
-      v.ldw = H;
+      v.nkt = H * esz / 128;
       v.width = w;
       if (FMT == FMT_MX) {
         v.sa = static_cast<const uint8_t*>(p.ws13_s) + (size_t)col0 * (H / 32);
         v.sb = static_cast<const uint8_t*>(p.ws13_s) + (size_t)(Is + col0) * (H / 32);
-        v.ldsc = H / 32;
       }
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws13_s)[0];
     } else {
-      v.wa = p.ws2 + (size_t)col0 * esz;
-      v.ldw = Is;
+      // K columns col0.. of W2: a K-tile offset into every row block
+      v.wa = p.ws2;
+      v.nkt = Is * esz / 128;
+      v.kt0 = col0 * esz / 128;
       v.width = w;
-      if (FMT == FMT_MX) {
-        v.sa = static_cast<const uint8_t*>(p.ws2_s) + col0 / 32;
-        v.ldsc = Is / 32;
-      }
+      if (FMT == FMT_MX) v.sa = static_cast<const uint8_t*>(p.ws2_s);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws2_s)[0];
     }
   }

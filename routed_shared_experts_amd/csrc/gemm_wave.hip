@@ -77,11 +77,11 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   // chunk are never stored) ----
   const uint8_t* wbase[NW];
   const uint8_t* sbase[NW];
-  wbase[0] = ev.wa + g * 16;
-  sbase[0] = ev.sa + g;
+  wbase[0] = ev.wa + lane * 16;
+  sbase[0] = ev.sa + lane;
   if constexpr (NW == 2) {
-    wbase[1] = ev.wb + g * 16;
-    sbase[1] = ev.sb + g;
+    wbase[1] = ev.wb + lane * 16;
+    sbase[1] = ev.sb + lane;
   }
   // ---- activations: this lane's token row through a buffer descriptor ----
   const bool xok = tok_l >= 0;
@@ -128,12 +128,14 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     const int cgi = t / nk, kt = t - cgi * nk;
     const int wrow = c0 + cgi * 16 + l16;
     const int row = (STAGE == 1 && wrow >= ev.width) ? 0 : wrow;
-    const size_t off = (size_t)row * ev.ldw * esz + (size_t)kt * 128;
+    // the wave's 16 rows of K tile kt: two contiguous 1024-byte halves
+    const size_t off = tile_off(ev, row / 16, kt);
+    const size_t soff = scale_tile_off(ev, row / 16, kt);
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
       wb[d][m][0] = ld16(wbase[m] + off);
-      wb[d][m][1] = ld16(wbase[m] + off + 64);
-      if constexpr (FMT == FMT_MX) wsc[d][m] = sbase[m][(size_t)row * ev.ldsc + kt * 4];
+      wb[d][m][1] = ld16(wbase[m] + off + 1024);
+      if constexpr (FMT == FMT_MX) wsc[d][m] = sbase[m][soff];
       else wsc[d][m] = 127;
     }
     if constexpr (kQuantA) {  // bf16 h: 32 bytes per 16-element chunk

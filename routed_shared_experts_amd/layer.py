@@ -9,8 +9,8 @@ import torch
 
 from . import (MoeForwardArgs, MoeWeights, MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_SCALE_NONE,
                MOE_SCALE_PER_EXPERT, MOE_SCALE_MX32, MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID,
-               SHARED_MODES, MOE_OK, MoeError, moe_validate, moe_workspace_bytes, moe_forward,
-               moe_status_str, _ptr)
+               MOE_LAYOUT_TILED, SHARED_MODES, MOE_OK, MoeError, moe_validate, moe_workspace_bytes,
+               moe_forward, moe_pack_weights, moe_pack_mx_scales, moe_status_str, _ptr)
 
 # layer format -> (x dtype, weight dtype, weight scale kind, output dtype)
 FORMATS = {
@@ -22,8 +22,22 @@ FORMATS = {
 
 
 def weights_struct(w13, w2, s13, s2, fmt):
+    """Weight family struct; the tensors must already be in the tiled layout."""
     _, wdt, wsc, _ = FORMATS[fmt]
-    return MoeWeights(_ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2), wdt, wsc)
+    return MoeWeights(_ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2), wdt, wsc, MOE_LAYOUT_TILED)
+
+
+def pack_weights(cfg, inp, stream=None):
+    """Tiled copies of the layer's weight matrices (and MX32 scale matrices),
+    made once at load time: {"w13", "w2", ["ws13", "ws2"], [scales]}.  Per-expert
+    scales and every non-weight input are used as they are."""
+    out = {}
+    names = ["w13", "w2"] + (["ws13", "ws2"] if cfg.I_s > 0 else [])
+    for n in names:
+        out[n] = moe_pack_weights(inp[n], stream=stream)
+        if cfg.fmt == "mxfp8":
+            out[n + "_scale"] = moe_pack_mx_scales(inp[n + "_scale"], stream=stream)
+    return out
 
 
 def forward_args(cfg, inp, out, shared_mode="auto", block_m=0):
@@ -54,12 +68,16 @@ def forward_args(cfg, inp, out, shared_mode="auto", block_m=0):
 class MoeLayer:
     """One configured layer forward on the current device.
 
-    Holds references to the input tensors (so the pointers stay valid), the
-    output tensor, the workspace, and, for the aux-stream mode, a second
-    stream and two events.
+    Holds references to the input tensors and the tiled weight copies (so the
+    pointers stay valid), the output tensor, the workspace, and, for the
+    aux-stream mode, a second stream and two events.
     """
 
-    def __init__(self, cfg, inp, shared_mode="auto", block_m=0, out=None):
+    def __init__(self, cfg, inp, shared_mode="auto", block_m=0, out=None, packed=None):
+        """inp: the workload's tensors with row-major weights; packed: their
+        tiled copies from pack_weights (made here when None)."""
+        packed = pack_weights(cfg, inp) if packed is None else packed
+        inp = dict(inp, **packed)
         self.cfg, self.inp = cfg, inp
         dev = inp["x"].device
         odt = torch.float32 if FORMATS[cfg.fmt][3] == MOE_F32 else torch.bfloat16

@@ -140,6 +140,13 @@ def test_validate_rejections():
     assert m.moe_validate(_args(q, "pseudo", I_s=4096)) == m.MOE_ERR_UNSUPPORTED  # row scale needs m == 1
     assert m.moe_validate(_args(q, "aux", I_s=4096)) == m.MOE_OK
     assert m.moe_validate(_args(q, x_row_scale=None)) == m.MOE_ERR_INVALID_ARG
+    # the kernels read tiled weights only
+    a = _args(c)
+    a.routed.layout = m.MOE_LAYOUT_ROW_MAJOR
+    assert m.moe_validate(a) == m.MOE_ERR_UNSUPPORTED
+    a = _args(c, "aux")
+    a.shared.layout = 7
+    assert m.moe_validate(a) == m.MOE_ERR_INVALID_ARG
 
 
 def test_forward_rejects_without_launching():
@@ -176,6 +183,15 @@ def test_step_entry_points_reject_bad_arguments():
     cap = m.moe_sort_capacity(8192, 9, 257, 128)
     assert L.moe_sort_tokens(p, 8192, 9, 257, 128, cap, p, p, p, p, p, p, big - 4, None, 0,
                              None) == m.MOE_ERR_WORKSPACE
+    # pack: rows % 16, row_bytes % 128, alignment, overlapping buffers
+    src, dst = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert L.moe_pack_weights(src, dst, 24, 256, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(src, dst, 32, 200, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(ctypes.c_void_p(0x100008), dst, 32, 256, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(src, ctypes.c_void_p(0x100000 + 32 * 256 - 16), 32, 256, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(src, dst, 0, 256, None) == m.MOE_OK  # nothing to do, no launch
+    assert L.moe_pack_mx_scales(src, dst, 16, 6, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_mx_scales(src, dst, 8, 8, None) == m.MOE_ERR_INVALID_ARG
     sa = m.MoeStageArgs()
     assert L.moe_stage1(ctypes.byref(sa), None) == m.MOE_ERR_INVALID_ARG
     assert L.moe_stage2_accum(None, None) == m.MOE_ERR_INVALID_ARG

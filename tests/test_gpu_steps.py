@@ -198,3 +198,39 @@ def test_mx_quant_bit_exact(gpu, T, H):
     rs, rq = oracle.mx_quantize(xb.float().numpy())
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rq)
+
+
+def _tiled_bytes(b, rows, row_bytes):
+    """The tiled layout of a row-major byte matrix, from its definition: tile
+    (row block, K tile) of 2048 bytes; chunk c = 4h + g of tile row r at
+    h * 1024 + (16 g + r) * 16."""
+    nkt = row_bytes // 128
+    t = b.reshape(rows // 16, 16, nkt, 2, 4, 16)          # [rb, r, kt, h, g, byte]
+    return t.transpose(0, 2, 3, 4, 1, 5).reshape(-1)       # [rb, kt, h, g, r, byte]
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(16, 64, torch.bfloat16), (48, 384, torch.bfloat16),
+                                             (32, 256, torch.float32), (64, 640, torch.uint8)])
+def test_pack_weights_bit_exact(gpu, rows, cols, dtype):
+    m = _m()
+    g = torch.Generator().manual_seed(rows * 1000 + cols)
+    raw = torch.randint(0, 256, (rows, cols * torch.empty((), dtype=dtype).element_size()), dtype=torch.uint8,
+                        generator=g)
+    src = raw.view(dtype).to(gpu)
+    dst = m.moe_pack_weights(src)
+    torch.cuda.synchronize()
+    got = dst.view(torch.uint8).cpu().numpy().reshape(-1)
+    exp = _tiled_bytes(raw.numpy(), rows, raw.shape[1])
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("rows,sb", [(16, 4), (48, 64), (32, 12)])
+def test_pack_mx_scales_bit_exact(gpu, rows, sb):
+    m = _m()
+    g = torch.Generator().manual_seed(rows + sb)
+    raw = torch.randint(0, 256, (rows, sb), dtype=torch.uint8, generator=g)
+    dst = m.moe_pack_mx_scales(raw.to(gpu))
+    torch.cuda.synchronize()
+    t = raw.numpy().reshape(rows // 16, 16, sb // 4, 4)    # [rb, r, kt, q]
+    exp = t.transpose(0, 2, 3, 1).reshape(-1)              # [rb, kt, q, r]
+    assert np.array_equal(dst.cpu().numpy().reshape(-1), exp)
