@@ -343,6 +343,12 @@ int32_t moe_query_feature(int32_t feature);
 /* Static string for a status code. */
 const char* moe_status_str(int32_t status);
 
+/* Description of the HIP error behind the last MOE_ERR_HIP returned to the
+ * calling thread ("" if none).  Every entry point that launches work first
+ * drops an error left pending by the caller's earlier runtime calls, so a
+ * MOE_ERR_HIP names a failure of this library's own calls. */
+const char* moe_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,8 @@ SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE
 # Exported symbols, in the order of include/moe.h.
 EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_route", "shared_gate_dot",
            "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_pack_weights", "moe_pack_mx_scales",
-           "moe_sort_tokens", "moe_stage1", "moe_stage2_accum", "moe_query_feature", "moe_status_str"]
+           "moe_sort_tokens", "moe_stage1", "moe_stage2_accum", "moe_query_feature", "moe_status_str",
+           "moe_last_hip_error"]
 
 c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
@@ -74,6 +75,11 @@ class MoeError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime under the same soname as /opt/rocm's; load
+    # it first so that the process has one runtime, the one torch's device
+    # memory and streams belong to (loading libmoe.so first would bind both to
+    # /opt/rocm's copy)
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
@@ -101,6 +107,7 @@ def _load():
         "moe_stage2_accum": (c_int32, [P(MoeStageArgs), c_void_p]),
         "moe_query_feature": (c_int32, [c_int32]),
         "moe_status_str": (ctypes.c_char_p, [c_int32]),
+        "moe_last_hip_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -122,7 +129,8 @@ def moe_status_str(status):
 
 def _check(status, what):
     if status != MOE_OK:
-        raise MoeError(f"{what} failed: {moe_status_str(status)}")
+        detail = f" ({_lib.moe_last_hip_error().decode()})" if status == MOE_ERR_HIP else ""
+        raise MoeError(f"{what} failed: {moe_status_str(status)}{detail}")
 
 
 def _ptr(t):

@@ -213,14 +213,30 @@ void fill_weights(GemmParams& g, const moe_weights& r, const moe_weights& s) {
   g.ws2_s = s.w2_scale;
 }
 
-#define HIP_TRY(x)                                  \
-  do {                                              \
-    if ((x) != hipSuccess) return MOE_ERR_HIP;      \
+thread_local hipError_t g_last_hip = hipSuccess;  // last HIP failure reported as MOE_ERR_HIP
+
+#define HIP_TRY(x)                     \
+  do {                                 \
+    const hipError_t e_ = (x);         \
+    if (e_ != hipSuccess) {            \
+      g_last_hip = e_;                 \
+      return MOE_ERR_HIP;              \
+    }                                  \
   } while (0)
+
+// Drops an error that earlier runtime calls of the caller left pending, so
+// that the hipGetLastError() after each launch here reports that launch.
+// (Errors from a faulted kernel are sticky and still surface.)
+inline void clear_pending_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
 extern "C" {
+
+const char* moe_last_hip_error(void) {
+  if (g_last_hip == hipSuccess) return "";
+  return hipGetErrorString(g_last_hip);
+}
 
 const char* moe_status_str(int32_t status) {
   switch (status) {
@@ -298,6 +314,7 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
   p.ids = topk_ids;
   p.w = topk_w;
   p.do_route = 1;
+  clear_pending_error();
   HIP_TRY(launch_route(p, stream));
   return MOE_OK;
 }
@@ -312,6 +329,7 @@ moe_status shared_gate_dot(const void* x, int32_t x_dtype, const void* g, int32_
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
+  clear_pending_error();
   HIP_TRY(launch_gate_dot(x, x_dtype == MOE_F32, g, T, H, apply_sigmoid, gate_out, stream));
   return MOE_OK;
 }
@@ -320,6 +338,7 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t ro
   if (!src || !dst || rows < 0 || row_bytes <= 0 || rows % 16 || row_bytes % 128) return MOE_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
   if (overlaps(src, dst, (size_t)rows * row_bytes)) return MOE_ERR_INVALID_ARG;
+  clear_pending_error();
   HIP_TRY(launch_pack_weights(src, dst, rows, row_bytes, stream));
   return MOE_OK;
 }
@@ -328,6 +347,7 @@ moe_status moe_pack_mx_scales(const void* src, void* dst, int64_t rows, int32_t 
   if (!src || !dst || rows < 0 || scale_bytes <= 0 || rows % 16 || scale_bytes % 4) return MOE_ERR_INVALID_ARG;
   if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u)) return MOE_ERR_INVALID_ARG;
   if (overlaps(src, dst, (size_t)rows * scale_bytes)) return MOE_ERR_INVALID_ARG;
+  clear_pending_error();
   HIP_TRY(launch_pack_scales(src, dst, rows, scale_bytes, stream));
   return MOE_OK;
 }
@@ -343,6 +363,7 @@ moe_status moe_quant_mx(const void* x, int32_t T, int32_t H, uint8_t* codes, uin
   p.xq = codes;
   p.xs = scales;
   p.do_route = 0;
+  clear_pending_error();
   HIP_TRY(launch_route(p, stream));
   return MOE_OK;
 }
@@ -377,6 +398,7 @@ moe_status moe_sort_tokens(const int32_t* topk_ids, int32_t T, int32_t k_total, 
   p.num_blocks = num_blocks;
   p.zero_ptr = static_cast<uint4*>(zero_ptr);
   p.zero_vec = (long long)(zero_bytes / 16);
+  clear_pending_error();
   HIP_TRY(launch_sort(p, stream));
   return MOE_OK;
 }
@@ -440,6 +462,7 @@ moe_status moe_stage1(const moe_stage_args* a, hipStream_t stream) {
   int fmt;
   moe_status st = stage_params(a, g, fmt);
   if (st != MOE_OK) return st;
+  clear_pending_error();
   HIP_TRY(launch_gemm(g, 1, fmt, 64, stream));
   return MOE_OK;
 }
@@ -461,6 +484,7 @@ moe_status moe_stage2_accum(const moe_stage_args* a, hipStream_t stream) {
   } else {
     return MOE_ERR_INVALID_ARG;
   }
+  clear_pending_error();
   if (a->addend_ready) HIP_TRY(hipStreamWaitEvent(stream, a->addend_ready, 0));
   HIP_TRY(launch_gemm(g, 2, fmt, 64, stream));
   return MOE_OK;
@@ -493,6 +517,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
 
   hipEvent_t* tev = a->timing_events;
+  clear_pending_error();
   if (tev) HIP_TRY(hipEventRecord(tev[0], main_s));
   // 1. prologue: routing (+ gate dot + MX quantisation of x)
   RouteParams rp{};

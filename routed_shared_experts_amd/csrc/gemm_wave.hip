@@ -3,16 +3,19 @@
 // Decode-sized batches (a few tokens per expert) make both stages stream the
 // expert weights once and do almost no arithmetic per byte (vLLM PR 65207's
 // decode profile is this regime).  A workgroup here is a single wave that owns
-// NCG consecutive 16-column groups of one block (stage 1: 2 groups = 32 h
-// columns, enough for one MX-32 block; stage 2: 4 groups = one 64-column
-// output tile).  Per group, stage 1 streams the 16 gate rows and the 16
-// matching up rows (SiLU-mul stays in registers) and stage 2 streams 16 rows
-// of W2; the prefetch runs on across group boundaries.  The weight rows are the MFMA M dimension and the block's (at most 16)
-// tokens the N dimension.  Weights go from HBM straight into MFMA operand
-// registers, D K-tiles ahead; the activation rows come from L2 through a
-// buffer descriptor (a padding row reads past the end of the buffer, i.e.
-// zeros, with no branch and no fetch).  There is no LDS and no barrier: the
-// many small independent workgroups hide each other's start-up latency.
+// NCG consecutive 16-column groups of one block: stage 1 owns 2 groups = 32 h
+// columns (one MX-32 block) and streams their gate and up rows, with SiLU-mul
+// in registers; stage 2 owns 4 groups = one 64-column output tile and streams
+// those 64 rows of W2.  The weight rows are the MFMA M dimension and the
+// block's (at most 16) tokens the N dimension.  The K tile is the outer loop:
+// each 128-byte activation tile is read once and feeds all NCG x (gate, up)
+// weight tiles.  Weights are in the tiled layout, so the wave's 16 rows of one
+// K tile are two contiguous 1024-byte loads, which go from HBM straight into
+// MFMA operand registers, D K-tiles ahead; the activation rows come from L2
+// through a buffer descriptor (a padding row reads past the end of the
+// buffer, i.e. zeros, with no branch and no fetch).  There is no LDS and no
+// barrier: the many small independent workgroups hide each other's start-up
+// latency.
 //
 // Stage 2 keeps the deterministic pair-row reduction: each wave stores the 64
 // columns of its weighted pair rows, then counts one arrival per token on the
@@ -27,6 +30,9 @@
 namespace moe {
 
 constexpr uint32_t kWvOutOfRange = 0x80000000u;  // buffer offset that reads as zero
+// prefetch depth caps (K tiles): stage 1 already has 2 groups x gate/up = 4
+// weight tiles per K tile in flight, stage 2 4 groups x W2
+constexpr int kWaveMaxDepth1 = 1, kWaveMaxDepth2 = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wv_rsrc(const void* base, uint32_t bytes) {
   // raw (untyped) buffer, dword 3 = 0x00020000 on gfx9-family parts
@@ -71,7 +77,6 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   if (STAGE == 1 && c0 >= ev.width) return;
   const int kbytes = (STAGE == 1) ? p.H * esz : ev.width * esz;  // a multiple of 128
   const int nk = kbytes / 128;                                    // a multiple of D (launch)
-  const int ntiles = NCG * nk;
 
   // ---- weights: lane row r = l16 of each group (clamped; rows past a narrow
   // chunk are never stored) ----
@@ -117,27 +122,9 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     }
   }
 
-  uint4 wb[D][NW][2];
-  int wsc[D][NW];
   uint4 xb[D][NX];
   int xsc[D];
-  // tile t = group * nk + k_tile; every load is unconditional (t clamped) so
-  // that no branch forces a wait for all outstanding loads
-  auto load = [&](int d, int t) {
-    t = t < ntiles ? t : ntiles - 1;
-    const int cgi = t / nk, kt = t - cgi * nk;
-    const int wrow = c0 + cgi * 16 + l16;
-    const int row = (STAGE == 1 && wrow >= ev.width) ? 0 : wrow;
-    // the wave's 16 rows of K tile kt: two contiguous 1024-byte halves
-    const size_t off = tile_off(ev, row / 16, kt);
-    const size_t soff = scale_tile_off(ev, row / 16, kt);
-#pragma unroll
-    for (int m = 0; m < NW; ++m) {
-      wb[d][m][0] = ld16(wbase[m] + off);
-      wb[d][m][1] = ld16(wbase[m] + off + 1024);
-      if constexpr (FMT == FMT_MX) wsc[d][m] = sbase[m][soff];
-      else wsc[d][m] = 127;
-    }
+  auto load_x = [&](int d, int kt) {
     if constexpr (kQuantA) {  // bf16 h: 32 bytes per 16-element chunk
       const uint32_t o = xoff + (uint32_t)kt * 256;
       xb[d][0] = wv_load16(xr, o);
@@ -154,12 +141,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     else
       xsc[d] = 127;
   };
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, d);
-
-  f32x4 acc[NW];
-  auto compute = [&](int d) {
-    uint4 x0, x1;
+  auto act = [&](int d, uint4& x0, uint4& x1) {
     if constexpr (kQuantA) {  // e4m3 with the row's 448 / amax on the fly
       uint32_t o[8];
 #pragma unroll
@@ -178,29 +160,63 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
       x0 = xb[d][0];
       x1 = xb[d][1];
     }
-#pragma unroll
-    for (int m = 0; m < NW; ++m) mfma_tile<FMT>(acc[m], wb[d][m][0], wb[d][m][1], x0, x1, wsc[d][m], xsc[d]);
+  };
+  // row block of group cgi (rows past a narrow chunk read row block 0 and are
+  // never stored)
+  auto group_rb = [&](int cgi) {
+    const int r0 = c0 + cgi * 16;
+    return (STAGE == 1 && r0 >= ev.width) ? 0 : r0 / 16;
   };
 
   // lane results: rows 4g..4g+3 of each group (columns c0 + 16 cgi + 4g + j),
   // token l16
   const float sc = rs * ev.wscale;
   float res[NCG][4];
+  // K tile outermost: one activation tile feeds every group of the wave;
+  // D K tiles of all NCG * NW weight tiles in flight
+  uint4 wb[D][NCG][NW][2];
+  int wsc[D][NCG][NW];
+  auto load = [&](int d, int kt) {
+    kt = kt < nk ? kt : nk - 1;  // unconditional loads: no branch forces a full wait
 #pragma unroll
-  for (int cgi = 0; cgi < NCG; ++cgi) {
+    for (int cgi = 0; cgi < NCG; ++cgi) {
+      const int rb = group_rb(cgi);
+      const size_t off = tile_off(ev, rb, kt);
 #pragma unroll
-    for (int m = 0; m < NW; ++m) acc[m] = f32x4{0, 0, 0, 0};
-    for (int kt0 = 0; kt0 < nk; kt0 += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        compute(d);
-        load(d, cgi * nk + kt0 + d + D);
+      for (int m = 0; m < NW; ++m) {
+        wb[d][cgi][m][0] = ld16(wbase[m] + off);
+        wb[d][cgi][m][1] = ld16(wbase[m] + off + 1024);
+        if constexpr (FMT == FMT_MX) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
+        else wsc[d][cgi][m] = 127;
       }
     }
+    load_x(d, kt);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, d);
+  f32x4 acc[NCG][NW];
+#pragma unroll
+  for (int cgi = 0; cgi < NCG; ++cgi)
+#pragma unroll
+    for (int m = 0; m < NW; ++m) acc[cgi][m] = f32x4{0, 0, 0, 0};
+  for (int kt0 = 0; kt0 < nk; kt0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      uint4 x0, x1;
+      act(d, x0, x1);
+#pragma unroll
+      for (int cgi = 0; cgi < NCG; ++cgi)
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+          mfma_tile<FMT>(acc[cgi][m], wb[d][cgi][m][0], wb[d][cgi][m][1], x0, x1, wsc[d][cgi][m], xsc[d]);
+      load(d, kt0 + d + D);
+    }
+  }
+#pragma unroll
+  for (int cgi = 0; cgi < NCG; ++cgi)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      res[cgi][j] = (STAGE == 1) ? silu_mul(acc[0][j] * sc, acc[NW - 1][j] * sc) : acc[0][j] * sc;
-  }
+      res[cgi][j] = (STAGE == 1) ? silu_mul(acc[cgi][0][j] * sc, acc[cgi][NW - 1][j] * sc) : acc[cgi][0][j] * sc;
 
   if constexpr (STAGE == 1) {
     const size_t slot = (size_t)slot_l;
@@ -320,8 +336,9 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   }
 }
 
-// Largest prefetch depth (4, 2 or 1) dividing the K-tile count of every
-// expert the launch can meet (routed width, shared width, last pseudo chunk).
+// Prefetch depth (2 or 1, within the stage's cap) dividing the K-tile count
+// of every expert the launch can meet (routed width, shared width, last
+// pseudo chunk).
 static int wave_depth(const GemmParams& p, int stage, int fmt) {
   const int esz = fmt == FMT_F32 ? 4 : (fmt == FMT_BF16 ? 2 : 1);
   int g = 0;
@@ -334,7 +351,8 @@ static int wave_depth(const GemmParams& p, int stage, int fmt) {
     g = p.I * esz / 128;
     if (p.n_pseudo > 0) g = gcd(g, (p.I_s - (p.n_pseudo - 1) * p.I) * esz / 128);
   }
-  return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int cap = stage == 1 ? kWaveMaxDepth1 : kWaveMaxDepth2;
+  return (g % 2 == 0 && cap >= 2) ? 2 : 1;
 }
 
 template <int FMT, int STAGE>
@@ -342,11 +360,10 @@ static hipError_t launch_wv(const GemmParams& p, int depth, hipStream_t s) {
   constexpr int CW = (STAGE == 1) ? 32 : 64;
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const dim3 grid((unsigned)(p.max_blocks * (width_max / CW)));
-  switch (depth) {
-    case 4: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 4>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 2>), grid, dim3(64), 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 1>), grid, dim3(64), 0, s, p); break;
-  }
+  if (depth >= 2)
+    hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 2>), grid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 1>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
