@@ -6,7 +6,16 @@ inputs already resident in HBM.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
                     [--mode auto|pseudo|aux|best] [--graph] [--no-cpu-baseline]
+                    [--copy-calibration MIB]
+
+Per-kernel durations come from HIP events that the layer records between its
+launches on every TIMING_EVERY-th step of the timed region (an event record
+costs a few microseconds, so recording them on every step would slow the step
+being measured).  --copy-calibration runs plain device copies of a known size
+after the timed region, for scaling the HBM byte counters of a profiler run.
 """
+
+import hashlib
 
 import argparse
 import json
@@ -23,6 +32,10 @@ METRIC = "MoE-layer tokens/s and achieved TFLOPS (% MFMA peak) / GB/s (% HBM) on
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "a8w8": 5000.0}
 DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "a8w8": "fp8-e4m3"}
+TIMING_EVERY = 8
+# sources of the GEMM kernels: the stage-1 traffic figure in profiles/ holds
+# only while their hash is the one it was measured with
+KERNEL_SOURCES = ["gemm_wave.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"]
 
 
 def parse():
@@ -36,7 +49,37 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
+                    help="after timing, copy MIB MiB device-to-device 4 times (profiler counter calibration)")
     return ap.parse_args()
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routed_shared_experts_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per stage-1 launch from the committed profiler summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_stage1_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic(cfg, ids, m_pseudo):
@@ -142,22 +185,21 @@ def main():
             el = time.perf_counter() - t0
             stage = None
         else:
-            # live per-kernel timing: events at the step boundaries on the main stream
-            handles = []
-            for e in evs:
-                arr = (m.c_void_p * 5)(*[x.cuda_event for x in e])
-                handles.append(arr)
+            # live per-kernel timing: events between the layer's launches on the
+            # main stream, on every TIMING_EVERY-th step
+            handles = [m.ctypes.cast((m.c_void_p * 5)(*[x.cuda_event for x in e]), m.c_void_p) for e in evs]
+            timed = [i for i in range(args.steps) if i % TIMING_EVERY == 0]
             t0 = time.perf_counter()
             for i in range(args.steps):
                 L = layers[i % copies]
-                L.args.timing_events = m.ctypes.cast(handles[i], m.c_void_p)
+                L.args.timing_events = handles[i] if i % TIMING_EVERY == 0 else None
                 L.forward()
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
             for L in layers:
                 L.args.timing_events = None
             names = ["prologue", "sort", "stage1", "stage2"]
-            stage = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+            stage = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in timed]))
                      for j, n in enumerate(names)}
         results[mode] = (el, stage, layers[0])
         del layers
@@ -202,8 +244,18 @@ def main():
         rec["kernels_ms"] = stage
         rec["roofline"] = {"kernel": "gemm stage 1 (routed gate/up + SiLU-mul)", "bound": "hbm",
                            "achieved": s1_bytes / (s1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": s1_bytes / (s1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                           "bytes_per_launch": s1_bytes, "flops_per_launch": s1_flops}
+                           "frac": s1_bytes / (s1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "traffic": measured_traffic(cfg.name) if best == "pseudo" else None,
+                           "bytes_per_launch": s1_bytes, "flops_per_launch": s1_flops,
+                           "timed_steps": len(range(0, args.steps, TIMING_EVERY))}
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 2**20) // 16 * 16
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
