@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.cpp", "route.hip", "sort.hip", "gemm.hip", "gemm_wave.hip", "pack.hip"]
+SOURCES = ["api.cpp", "route.hip", "sort.hip", "gemm.hip", "gemm_wave.hip", "gemm_tile.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -180,7 +180,7 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_acc = take(aux ? (size_t)a->T * a->H * 4 : 0);
   pl.off_pair = take((size_t)P * a->H * 4);
   // cleared by the sort launch: arrival counters, then the routed row amax (A8W8)
-  pl.off_cnt = take((size_t)a->T * (a->H / 64) * 4);
+  pl.off_cnt = take(moe_stage2_counters(a->T, a->H) * 4);
   pl.off_amax = take(fmt == FMT_A8W8 ? (size_t)pl.capacity * 4 : 0);
   pl.off_end = o;
   pl.zero_begin = pl.off_cnt;

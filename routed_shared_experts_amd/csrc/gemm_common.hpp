@@ -1,8 +1,9 @@
-// Pieces shared by the grouped-GEMM kernels (gemm.hip: LDS-staged tiles for
-// many rows per expert; gemm_skinny.hip: 16-row blocks with weights streamed
-// straight into MFMA operand registers): operand formats, the MFMA wrapper,
-// the expert/pseudo-expert resolution, the per-block row setup and the two
-// epilogues.
+// Pieces shared by the grouped-GEMM kernels (gemm.hip: LDS-staged tiles, the
+// general fallback; gemm_wave.hip: 16-row blocks, one wave per workgroup with
+// weights streamed straight into MFMA operand registers; gemm_tile.hip: 32-128
+// row blocks, weights in registers and token rows staged through LDS): operand
+// formats, the MFMA wrapper, the expert/pseudo-expert resolution, the
+// per-block row setup, the epilogues and the last-arrival reduction.
 #pragma once
 
 #include "common.hpp"
@@ -298,6 +299,58 @@ __device__ __forceinline__ void epilogue_stage2(const GemmParams& p, const float
       else
         static_cast<float*>(p.out)[(size_t)tok * p.H + n0 + c] = v;
     }
+  }
+}
+
+// Last arrival at a (token, 64-column tile): the addend plus the token's
+// k_total weighted pair rows, summed in slot order in fp32 and rounded once
+// into out.  The calling lane covers the 16 columns from cbase.  Pair rows
+// are read with device-coherent loads (they were written from other XCDs),
+// four rows per round trip.
+__device__ __forceinline__ void last_arrival_sum16(const GemmParams& p, int tok, int cbase) {
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = p.acc ? p.acc[(size_t)tok * p.H + cbase + q] : 0.0f;
+  const uint64_t* rows = reinterpret_cast<const uint64_t*>(p.pair_out + (size_t)tok * p.k_total * p.H + cbase);
+  const size_t rstride = (size_t)(p.H / 2);  // one pair row, in 8-byte words
+  int jj = 0;
+  for (; jj + 4 <= p.k_total; jj += 4) {
+    uint64_t t[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        t[r][q] = __hip_atomic_load(rows + (jj + r) * rstride + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[2 * q] += __uint_as_float((uint32_t)t[r][q]);
+        v[2 * q + 1] += __uint_as_float((uint32_t)(t[r][q] >> 32));
+      }
+  }
+  for (; jj < p.k_total; ++jj) {
+    uint64_t t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      t[q] = __hip_atomic_load(rows + jj * rstride + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v[2 * q] += __uint_as_float((uint32_t)t[q]);
+      v[2 * q + 1] += __uint_as_float((uint32_t)(t[q] >> 32));
+    }
+  }
+  if (p.out_bf16) {
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok * p.H + cbase);
+    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok * p.H + cbase);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
 }
 

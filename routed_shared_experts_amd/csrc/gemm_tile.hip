@@ -1,0 +1,622 @@
+// Grouped GEMM for sorted blocks of 32-128 rows (gfx950), both stages.
+//
+// Stage 1 computes a = x_gathered . W13[e]^T, applies the per-token and
+// per-expert scales to the fp32 accumulator (MX-32 block scales inside the
+// block-scaled MFMA), then h = SiLU(a_gate) * a_up, rounded or quantised to
+// the stage-2 input format (AITER PR 6106, "Technical Details"; vLLM PR 65207,
+// "Purpose", commit 2 for the two-stage structure).  Stage 2 computes
+// o = h . W2[e]^T with the same scale rules and hands the weighted pair rows to
+// the deterministic last-arrival reduction onto the shared-expert addend
+// (vLLM PR 65207, commit 2: the shared output is accumulated in stage 2), or in
+// STORE mode writes gamma_t * o as the dense addend.
+//
+// Mapping.  The expert weights are the MFMA "A" operand (M = weight rows) and
+// the block's tokens the "B" operand (N = tokens).  The tiled weight layout
+// (16-row x 128-byte tiles, two 1 KiB halves in operand order) means one wave
+// loads a 16-row fragment of a K tile as two contiguous 1 KiB reads straight
+// into MFMA operand registers: weights never pass through LDS, and no two
+// waves load the same weight bytes.  The gathered token rows are shared by the
+// four waves, so they are staged through LDS, double buffered, in the same
+// operand order (each 16-row x 128-byte fragment is 2 KiB, lane-contiguous),
+// which makes both the LDS writes and the ds_read_b128 fragment reads free of
+// bank conflicts without a swizzle.
+//
+// Workgroup = 4 waves x 64 weight rows: in stage 1 a wave owns 32 h columns
+// (32 gate rows + the matching 32 up rows, so SiLU-mul happens in registers),
+// in stage 2 one 64-column reduction tile.  Per wave and K tile (128 bytes of
+// K): 8 x 16 B weight loads per lane issued one tile ahead, 2 x NB fragment
+// reads from LDS, and 4 x NB MFMA tiles.
+//
+// Placement.  Workgroups are dealt round-robin to the eight XCDs.  Stage 1
+// remaps launch order so that consecutive logical tiles (the column tiles of
+// one block, then the next block of the same expert) share one XCD's L2.
+// Stage 2 (ACCUMULATE) runs persistent workgroups that take work from one
+// queue per XCD: queue x holds the 64-column reduction tiles t = x (mod 8) of
+// every block, and a workgroup reads the XCD it actually runs on from the
+// XCC_ID hardware register, so every writer and the last-arrival reader of a
+// (token, tile) run on the same XCD.  Their pair rows then meet in that XCD's
+// L2 with ordinary stores and loads; cross-XCD coherence is needed only for
+// the counters (device-scope atomics).  A queue is claimed by the first XCD
+// that touches it; an XCD whose own workgroups never arrive has its queue
+// claimed and drained by another, which keeps the property.
+#include "gemm_common.hpp"
+
+namespace moe {
+
+constexpr int kTileThreads = 256;
+constexpr int kNumXcd = 8;
+constexpr uint32_t kTileOutOfRange = 0x80000000u;  // buffer offset past every range: reads zero
+
+// Bijection of [0, active) that gives each XCD (blockIdx % 8) a contiguous
+// range of logical tile indices.
+__device__ __forceinline__ int xcd_remap(int bid, int active) {
+  const int q = active / kNumXcd, r = active % kNumXcd;
+  const int x = bid % kNumXcd, i = bid / kNumXcd;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// The XCD this wave runs on (HW_REG_XCC_ID, bits 2:0).
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & (kNumXcd - 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  // raw (untyped) buffer, dword 3 = 0x00020000 on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+template <int BM>
+struct TileSmem {
+  uint8_t x[2][BM * 128];  // staged token rows, operand order
+  uint32_t xsc[2][BM];     // MX: the rows' e8m0 scales of the staged K tile
+  int tok[BM];
+  int pair[BM];
+  float rw[BM];   // stage 2: pair weight / gate
+  float rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
+  float inv[BM];  // stage 2 A8W8: 448 / amax
+  int item;       // persistent stage 2: the claimed work item / queue
+};
+
+// Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
+// k_total pair rows in slot order, one rounding.  Same arithmetic as
+// last_arrival_sum16, read with ordinary loads: every pair row of the tile was
+// written through this XCD's L2, and each line is read once.
+__device__ __forceinline__ void last_arrival_sum16_xcd(const GemmParams& p, int tok, int cbase) {
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 a = p.acc ? *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + cbase + 4 * q)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * q] = a.x;
+    v[4 * q + 1] = a.y;
+    v[4 * q + 2] = a.z;
+    v[4 * q + 3] = a.w;
+  }
+  const float* rows = p.pair_out + (size_t)tok * p.k_total * p.H + cbase;
+  int jj = 0;
+  for (; jj + 4 <= p.k_total; jj += 4) {
+    float4 t[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[r][q] = *reinterpret_cast<const float4*>(rows + (size_t)(jj + r) * p.H + 4 * q);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[4 * q] += t[r][q].x;
+        v[4 * q + 1] += t[r][q].y;
+        v[4 * q + 2] += t[r][q].z;
+        v[4 * q + 3] += t[r][q].w;
+      }
+  }
+  for (; jj < p.k_total; ++jj) {
+    float4 t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const float4*>(rows + (size_t)jj * p.H + 4 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[4 * q] += t[q].x;
+      v[4 * q + 1] += t[q].y;
+      v[4 * q + 2] += t[q].z;
+      v[4 * q + 3] += t[q].w;
+    }
+  }
+  if (p.out_bf16) {
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok * p.H + cbase);
+    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok * p.H + cbase);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+}
+
+// One block b of expert view ev: this wave's columns start at c0 (stage 1: h
+// columns c0..c0+31; stage 2: output columns c0..c0+63); waves with
+// wave_ok = false take part in the staging and barriers but store nothing.
+// Starts by filling the row tables (the caller synchronises before reusing
+// the shared memory).
+template <int FMT, int STAGE, int NB>
+__device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB>& sm, int b, const ExpertView& ev,
+                                           int c0, bool wave_ok) {
+  constexpr int esz = FmtInfo<FMT>::esz;
+  constexpr int BM = 16 * NB;                                // sorted rows of a block
+  constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);  // bf16 h quantised while staged
+  constexpr int XG = kQuantA ? 2 : 1;                        // 16-byte global loads per staged chunk
+  constexpr int CPT = NB / 2;                                // staged 16-byte chunks per thread per K tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int g = lane / 16, l16 = lane % 16;
+
+  setup_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, sm.rw, sm.rs, sm.inv);
+  __syncthreads();
+
+  // K extent in bytes of the staged (MFMA) format; a multiple of 128
+  const int kbytes = (STAGE == 1) ? p.H * esz : ev.width * esz;
+  const int nk = kbytes / 128;
+
+  // ---- this wave's weight fragments: 4 row blocks of 16, addressed as
+  // (uniform tile offset, lane * 16) in a buffer over the matrix ----
+  __amdgpu_buffer_rsrc_t wrs[2], srs[2];
+  uint32_t wtile[4], stile[4];
+  wrs[0] = tile_rsrc(ev.wa, 0x7FFFFFFF);
+  wrs[1] = tile_rsrc((STAGE == 1) ? ev.wb : ev.wa, 0x7FFFFFFF);
+  if constexpr (FMT == FMT_MX) {
+    srs[0] = tile_rsrc(ev.sa, 0x7FFFFFFF);
+    srs[1] = tile_rsrc((STAGE == 1) ? ev.sb : ev.sa, 0x7FFFFFFF);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    // stage 1: gate rows c0.., c0+16.. then the same up rows
+    const int rb = (STAGE == 1) ? c0 / 16 + (mb & 1) : c0 / 16 + mb;
+    wtile[mb] = (uint32_t)tile_off(ev, rb, 0);
+    stile[mb] = (uint32_t)scale_tile_off(ev, rb, 0);
+  }
+  const uint32_t wlane = (uint32_t)lane * 16;
+
+  // ---- staged token rows: chunk q = tid + 256 u is (row block q/128, half,
+  // lane group, row) in operand order; padding rows read past the buffer ----
+  __amdgpu_buffer_rsrc_t xrs, xsrs;
+  if (STAGE == 1) {
+    xrs = tile_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * esz));
+    if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
+  } else {
+    const size_t rows = (size_t)p.max_blocks * BM;
+    xrs = tile_rsrc(p.h, (uint32_t)(rows * p.ld_h * (kQuantA ? 2 : esz)));
+    if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
+  }
+  uint32_t xoff[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int q = tid + kTileThreads * u;
+    const int r = (q / 128) * 16 + (q % 16);
+    const int c = ((q / 64) % 2) * 4 + (q / 16) % 4;  // 16-byte chunk of the 128-byte K tile
+    const int tok = sm.tok[r];
+    if (tok < 0) {
+      xoff[u] = kTileOutOfRange;
+    } else if (STAGE == 1) {
+      xoff[u] = (uint32_t)((size_t)tok * p.H * esz) + c * 16;
+    } else {
+      xoff[u] = (uint32_t)(((size_t)b * BM + r) * p.ld_h * (kQuantA ? 2 : esz)) + c * 16 * XG;
+    }
+  }
+  uint32_t xsoff = kTileOutOfRange;  // the row's e8m0 scales (MX), for threads tid < BM
+  if (FMT == FMT_MX && tid < BM && sm.tok[tid] >= 0)
+    xsoff = (STAGE == 1) ? (uint32_t)(sm.tok[tid] * (p.H / 32)) : (uint32_t)((b * BM + tid) * (p.ld_h / 32));
+
+  auto load_w = [&](uint4 (&w)[4][2], int (&sc)[4], int kt) {
+    kt = kt < nk ? kt : nk - 1;  // past the end: a harmless reload of the last tile
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const __amdgpu_buffer_rsrc_t r = wrs[mb >> 1];
+      const uint32_t so = wtile[mb] + (uint32_t)kt * 2048;
+      w[mb][0] = tile_load16(r, wlane, so);
+      w[mb][1] = tile_load16(r, wlane + 1024, so);
+      if constexpr (FMT == FMT_MX)
+        sc[mb] = (int)__builtin_amdgcn_raw_buffer_load_b8(srs[mb >> 1], (int)lane, (int)(stile[mb] + kt * 64), 0);
+      else
+        sc[mb] = 127;
+    }
+  };
+
+  uint4 xr[CPT][XG];
+  uint32_t xsr = 0;
+  auto load_x = [&](int kt) {
+    kt = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+#pragma unroll
+      for (int h = 0; h < XG; ++h) xr[u][h] = tile_load16(xrs, xoff[u] + h * 16, (uint32_t)kt * 128 * XG);
+    if constexpr (FMT == FMT_MX) {
+      if (tid < BM) xsr = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + kTileThreads * u;
+      uint4 v;
+      if constexpr (kQuantA) {
+        const float inv = sm.inv[(q / 128) * 16 + (q % 16)];
+        const uint32_t w[8] = {xr[u][0].x, xr[u][0].y, xr[u][0].z, xr[u][0].w,
+                               xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          o[t] = pack4_e4m3(bf16_to_f32(w[2 * t] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t] >> 16) * inv,
+                            bf16_to_f32(w[2 * t + 1] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t + 1] >> 16) * inv);
+        v = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        v = xr[u][0];
+      }
+      *reinterpret_cast<uint4*>(&sm.x[buf][q * 16]) = v;
+    }
+    if constexpr (FMT == FMT_MX) {
+      if (tid < BM) sm.xsc[buf][tid] = xsr;
+    }
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0, 0, 0, 0};
+
+  auto compute = [&](int buf, const uint4 (&w)[4][2], const int (&sc)[4]) {
+    if constexpr (FMT == FMT_BF16) {
+      // two K=32 halves; the half is the outer loop so that consecutive MFMAs
+      // update different accumulators
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + h * 1024 + lane * 16]);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[mb][h]),
+                                                                  __builtin_bit_cast(bf16x8, bf), acc[mb][nb], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint8_t* frag = &sm.x[buf][nb * 2048 + lane * 16];
+        const uint4 b0 = *reinterpret_cast<const uint4*>(frag);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(frag + 1024);
+        const int sb = (FMT == FMT_MX) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) mfma_tile<FMT>(acc[mb][nb], w[mb][0], w[mb][1], b0, b1, sc[mb], sb);
+      }
+    }
+  };
+
+  // Two weight register sets and two LDS buffers in ping-pong: while K tile
+  // kt is multiplied, the weights of kt + 1 are in flight (issued one step
+  // earlier) and the token rows of kt + 1 are loaded and then staged.  Every
+  // step is unconditional; loads past the end reload the last tile.
+  uint4 wA[4][2], wB[4][2];
+  int sA[4], sB[4];
+  load_w(wA, sA, 0);
+  load_w(wB, sB, 1);
+  load_x(0);
+  store_x(0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    load_x(kt + 1);
+    compute(0, wA, sA);
+    load_w(wA, sA, kt + 2);
+    store_x(1);
+    __syncthreads();
+    load_x(kt + 2);
+    compute(1, wB, sB);
+    load_w(wB, sB, kt + 3);
+    store_x(0);
+    __syncthreads();
+  }
+  if (kt < nk) compute(0, wA, sA);  // odd tile count: the last tile sits in buffer 0 / set A
+
+  // ---- epilogues (per wave, from registers) ----
+  // acc[mb][nb][v] = row (mb, 4g + v) of the wave's weight rows x token row nb*16 + l16
+  if (!wave_ok) return;
+  if constexpr (STAGE == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = nb * 16 + l16;
+      const int tok = sm.tok[r];
+      const size_t slot = (size_t)b * BM + r;
+      const float sc = sm.rs[r] * ev.wscale;
+      float hv[2][4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hv[m][v] = silu_mul(acc[m][nb][v] * sc, acc[m + 2][nb][v] * sc);
+      if constexpr (FMT == FMT_MX) {
+        // the wave's 32 columns are one MX-32 block of the token's h row
+        float amax = 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hv[m][v] = bf16_to_f32(f32_to_bf16(hv[m][v]));
+            amax = fmaxf(amax, fabsf(hv[m][v]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+        int X = (eb == 0) ? -127 : (eb - 127 - 8);
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        const float mul = __builtin_ldexpf(1.0f, -X);
+        if (tok >= 0) {
+          uint8_t* dst = p.h + slot * p.ld_h + c0 + 4 * g;
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            *reinterpret_cast<uint32_t*>(dst + 16 * m) =
+                pack4_e4m3(hv[m][0] * mul, hv[m][1] * mul, hv[m][2] * mul, hv[m][3] * mul);
+          if (g == 0) static_cast<uint8_t*>(p.h_s)[slot * (p.ld_h / 32) + c0 / 32] = (uint8_t)(X + 127);
+        }
+      } else {
+        float amax = 0.f;
+        uint32_t bits[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            bits[m][v] = f32_to_bf16(hv[m][v]);
+            amax = fmaxf(amax, fabsf(bf16_to_f32(bits[m][v])));
+          }
+        if (tok >= 0) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.h) + slot * p.ld_h + c0 + 4 * g;
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            *reinterpret_cast<uint2*>(dst + 16 * m) =
+                make_uint2(bits[m][0] | (bits[m][1] << 16), bits[m][2] | (bits[m][3] << 16));
+        }
+        if constexpr (FMT == FMT_A8W8) {
+          // row amax of the bf16-rounded values over the wave's 32 columns
+          amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+          if (g == 0 && tok >= 0) atomicMax(reinterpret_cast<unsigned int*>(p.h_s) + slot, __float_as_uint(amax));
+        }
+      }
+    }
+  } else {
+    if (p.mode == 0) {  // STORE: gamma * S(x), the dense shared expert's addend
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + l16;
+        const int tok = sm.tok[r];
+        if (tok < 0) continue;
+        const float sc = sm.rs[r] * ev.wscale;
+        const float gm = p.gamma ? p.gamma[tok] : 1.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          *reinterpret_cast<float4*>(p.acc + (size_t)tok * p.H + c0 + mb * 16 + 4 * g) =
+              make_float4(gm * (acc[mb][nb][0] * sc), gm * (acc[mb][nb][1] * sc), gm * (acc[mb][nb][2] * sc),
+                          gm * (acc[mb][nb][3] * sc));
+      }
+      return;
+    }
+    // ACCUMULATE: the weighted pair rows (64 columns each); the tile's
+    // reduction is XCD-local, so ordinary stores
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = nb * 16 + l16;
+      const int pair = sm.pair[r];
+      if (pair < 0) continue;
+      const float sc = sm.rs[r] * ev.wscale;
+      const float wgt = sm.rw[r];
+      float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        *reinterpret_cast<float4*>(dst + mb * 16) =
+            make_float4(wgt * (acc[mb][nb][0] * sc), wgt * (acc[mb][nb][1] * sc), wgt * (acc[mb][nb][2] * sc),
+                        wgt * (acc[mb][nb][3] * sc));
+    }
+    // count arrivals once the stores have reached the L2 (their acknowledgement);
+    // all of the block's counter atomics are issued before any result is used
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    const int n_tiles = p.H / 64;
+    const int tile = c0 / 64;
+    int old[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = nb * 16 + l16;
+      old[nb] = -1;
+      if (g == 0 && sm.pair[r] >= 0) old[nb] = atomicAdd(p.counters + (size_t)sm.tok[r] * n_tiles + tile, 1);
+    }
+    // done bits of the block's (row block, token) slots, spread to the token's four lanes
+    uint32_t done = 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) done |= (uint32_t)(__shfl(old[nb], l16, kWave) == p.expected - 1) << nb;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // the wave's last arrivals, compacted 16 at a time: entry i -> lanes
+    // (g, i % 16), each summing 16 of the tile's 64 columns
+    if (__ballot(done != 0)) {
+      uint32_t cnt[NB];
+      int total = 0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        // 16-bit mask of the row block's done tokens (lanes 0..15 hold them)
+        cnt[nb] = (uint32_t)__ballot(((done >> nb) & 1u) != 0 && g == 0) & 0xFFFFu;
+        total += __popc(cnt[nb]);
+      }
+      for (int base = 0; base < total; base += 16) {
+        const int i = base + l16;
+        if (i < total) {
+          // the i-th done slot in (row block, token) order
+          int rem = i, r = -1;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int c = __popc(cnt[nb]);
+            if (r < 0 && rem < c) {
+              uint32_t m = cnt[nb];
+              for (int k = 0; k < rem; ++k) m &= m - 1;  // drop the lowest rem set bits
+              r = nb * 16 + (__ffs(m) - 1);
+            }
+            if (r < 0) rem -= c;
+          }
+          last_arrival_sum16_xcd(p, sm.tok[r], c0 + 16 * g);
+        }
+      }
+    }
+  }
+}
+
+// Waves per SIMD the register allocation targets: two workgroups per CU keep
+// twice the loads in flight, where the operand registers allow it without
+// spilling (bf16; a8w8 except the 128-row stage 2, which also quantises h
+// while staging it; 32-row blocks).
+template <int FMT, int STAGE, int NB>
+constexpr int tile_waves_per_eu() {
+  return (FMT == FMT_BF16 || (FMT == FMT_A8W8 && (STAGE == 1 || NB <= 4)) || NB <= 2) ? 2 : 1;
+}
+
+// Stage 1 (and the dense STORE stage 2): one workgroup per (block, column
+// tile) of 128 h columns / 256 output columns.
+template <int FMT, int STAGE, int NB>
+__global__ __launch_bounds__(kTileThreads)
+__attribute__((amdgpu_waves_per_eu(tile_waves_per_eu<FMT, STAGE, NB>(), tile_waves_per_eu<FMT, STAGE, NB>())))
+void gemm_tile_kernel(GemmParams p) {
+  constexpr int BM = 16 * NB;
+  constexpr int WCOLS = (STAGE == 1) ? 128 : 256;
+  __shared__ __attribute__((aligned(16))) TileSmem<BM> sm;
+
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // uniform: weight offsets stay scalar
+  const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
+  const int n_col = width_max / WCOLS;
+  const int nblk = p.dense ? (p.T + BM - 1) / BM : *p.num_blocks;
+  const int active = nblk * n_col;
+  if ((int)blockIdx.x >= active) return;
+  const int lt = (STAGE == 1) ? xcd_remap((int)blockIdx.x, active) : (int)blockIdx.x;
+  const int b = lt / n_col, nc = lt % n_col;
+  const int n0 = nc * WCOLS;
+
+  const int e = p.dense ? -1 : p.block_expert[b];
+  const ExpertView ev = resolve_expert<FMT, STAGE>(p, e);
+  if (STAGE == 1 && n0 >= ev.width) return;  // past a narrow pseudo-expert chunk (uniform)
+  int c0 = n0 + wv * ((STAGE == 1) ? 32 : 64);
+  const bool wave_ok = (STAGE == 1) ? (c0 < ev.width) : true;
+  if (!wave_ok) c0 = 0;  // rows past a narrow chunk: read block 0, store nothing
+  tile_block<FMT, STAGE, NB>(p, sm, b, ev, c0, wave_ok);
+}
+
+// Stage 2 ACCUMULATE: persistent workgroups draining the per-XCD queues.
+// Queue x's items are (block b, group j): its waves own the reduction tiles
+// t = x + 8 (4 j + w), w = 0..3 (t < H/64).  Queue state (next item, owner)
+// follows the T * (H/64) arrival counters and is zero on entry.
+template <int FMT, int NB>
+__global__ __launch_bounds__(kTileThreads)
+__attribute__((amdgpu_waves_per_eu(tile_waves_per_eu<FMT, 2, NB>(), tile_waves_per_eu<FMT, 2, NB>())))
+void gemm_tile_accum_kernel(GemmParams p) {
+  constexpr int BM = 16 * NB;
+  __shared__ __attribute__((aligned(16))) TileSmem<BM> sm;
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n64 = p.H / 64;
+  const int nblk = *p.num_blocks;
+  int* q_next = p.counters + (size_t)p.T * n64;
+  int* q_owner = q_next + kNumXcd;
+  const int me = xcc_id();
+
+  for (int step = 0; step < kNumXcd; ++step) {
+    const int q = (me + step) % kNumXcd;
+    const int tiles_q = (n64 - q + kNumXcd - 1) / kNumXcd;  // t = q (mod 8), t < n64
+    const int groups_q = (tiles_q + 3) / 4;
+    const int items_q = nblk * groups_q;
+    if (items_q <= 0) continue;
+    // claim the queue for this XCD (or find it already ours)
+    if (tid == 0) {
+      const int o = atomicCAS(q_owner + q, 0, me + 1);
+      sm.item = (o == 0 || o == me + 1) ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ours = sm.item != 0;
+    __syncthreads();
+    if (!ours) continue;
+    for (;;) {
+      if (tid == 0) sm.item = atomicAdd(q_next + q, 1);
+      __syncthreads();
+      const int it = sm.item;
+      __syncthreads();
+      if (it >= items_q) break;
+      const int b = it / groups_q, j = it % groups_q;
+      const int t = q + kNumXcd * (4 * j + wv);
+      const bool wave_ok = t < n64;
+      const ExpertView ev = resolve_expert<FMT, 2>(p, p.block_expert[b]);
+      tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok);
+      __syncthreads();  // the next item rewrites the row tables
+    }
+  }
+}
+
+// Stage 1 needs whole 128-column workgroups (and 32-column waves for a
+// narrow last pseudo-expert chunk); stage 2 whole 256-column workgroups in
+// STORE mode and 64-column tiles in ACCUMULATE mode.  The token rows are
+// addressed with 32-bit buffer offsets.
+bool tile_kernel_fits(const GemmParams& p, int stage, int fmt) {
+  if (fmt == FMT_F32) return false;
+  if (p.block_m != 32 && p.block_m != 64 && p.block_m != 128) return false;
+  const size_t esz = fmt == FMT_BF16 ? 2 : 1;
+  const size_t hsz = fmt == FMT_A8W8 ? 2 : esz;
+  if (stage == 1) {
+    const int w = p.dense ? p.I_s : p.I;
+    if (w % 128) return false;
+    if (!p.dense && p.n_pseudo > 0 && p.I_s % 32) return false;
+    return (size_t)p.T * p.H * esz < 0x7FFFFFFFu;
+  }
+  if (p.mode == 0 ? p.H % 256 : p.H % 64) return false;
+  return (size_t)p.max_blocks * p.block_m * p.ld_h * hsz < 0x7FFFFFFFu;
+}
+
+template <int FMT, int STAGE, int NB>
+static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
+  if (STAGE == 2 && p.mode != 0) {
+    // persistent: two workgroups per CU of each XCD at most (an XCD has 32
+    // CUs), no more than the largest queue has items
+    const int n64 = p.H / 64;
+    const int groups = ((n64 + kNumXcd - 1) / kNumXcd + 3) / 4;
+    long long per_xcd = (long long)p.max_blocks * groups;
+    if (per_xcd > 64) per_xcd = 64;
+    hipLaunchKernelGGL((gemm_tile_accum_kernel<FMT, NB>), dim3((unsigned)(kNumXcd * per_xcd)), dim3(kTileThreads), 0, s,
+                       p);
+    return hipGetLastError();
+  }
+  constexpr int WCOLS = (STAGE == 1) ? 128 : 256;
+  const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
+  const dim3 grid((unsigned)(p.max_blocks * (width_max / WCOLS)));
+  hipLaunchKernelGGL((gemm_tile_kernel<FMT, STAGE, NB>), grid, dim3(kTileThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int FMT, int STAGE>
+static hipError_t launch_tile_fs(const GemmParams& p, hipStream_t s) {
+  switch (p.block_m) {
+    case 32: return launch_tile_nb<FMT, STAGE, 2>(p, s);
+    case 64: return launch_tile_nb<FMT, STAGE, 4>(p, s);
+    case 128: return launch_tile_nb<FMT, STAGE, 8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_tile(const GemmParams& p, int stage, int fmt, hipStream_t s) {
+  switch (fmt) {
+    case FMT_BF16: return stage == 1 ? launch_tile_fs<FMT_BF16, 1>(p, s) : launch_tile_fs<FMT_BF16, 2>(p, s);
+    case FMT_MX: return stage == 1 ? launch_tile_fs<FMT_MX, 1>(p, s) : launch_tile_fs<FMT_MX, 2>(p, s);
+    case FMT_A8W8: return stage == 1 ? launch_tile_fs<FMT_A8W8, 1>(p, s) : launch_tile_fs<FMT_A8W8, 2>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -302,37 +302,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
       done = (old == p.expected - 1);
     }
     done = __shfl(done, l16, kWave);  // broadcast to the token's 4 lanes
-    if (done) {
-      // last arrival: addend + rows in slot order; this lane sums 16 columns
-      const int cbase = c0 + 16 * g;
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) v[q] = p.acc ? p.acc[(size_t)tok_l * p.H + cbase + q] : 0.0f;
-      const uint64_t* rows = reinterpret_cast<const uint64_t*>(p.pair_out + (size_t)tok_l * p.k_total * p.H + cbase);
-      for (int jj = 0; jj < p.k_total; ++jj) {
-        uint64_t t[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          t[q] = __hip_atomic_load(rows + (size_t)jj * (p.H / 2) + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          v[2 * q] += __uint_as_float((uint32_t)t[q]);
-          v[2 * q + 1] += __uint_as_float((uint32_t)(t[q] >> 32));
-        }
-      }
-      if (p.out_bf16) {
-        uint32_t w[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
-        uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok_l * p.H + cbase);
-        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      } else {
-        float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok_l * p.H + cbase);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      }
-    }
+    if (done) last_arrival_sum16(p, tok_l, c0 + 16 * g);
   }
 }
 

@@ -81,6 +81,8 @@ size_t sort_scratch_bytes(int P, int n_experts);
 hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s);
 hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t s);
 bool wave_kernel_fits(const GemmParams& p, int stage, int fmt);
+hipError_t launch_gemm_tile(const GemmParams& p, int stage, int fmt, hipStream_t s);
+bool tile_kernel_fits(const GemmParams& p, int stage, int fmt);
 hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes, hipStream_t s);
 hipError_t launch_pack_scales(const void* src, void* dst, int64_t rows, int32_t scale_bytes, hipStream_t s);
 

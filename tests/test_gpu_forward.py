@@ -27,12 +27,14 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("block_m", [0, 16])
+@pytest.mark.parametrize("block_m", [0, 16, 32, 128])
 @pytest.mark.parametrize("mode", ["pseudo", "aux"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layers_all_outputs(gpu, name, mode, block_m):
-    """block_m = 16 takes the register-streamed (skinny) GEMM kernels, the
-    automatic choice takes the LDS-staged ones at these sizes."""
+    """block_m = 16 takes the one-wave register-streamed GEMM kernels; 32-128
+    take the tiled kernels (weights in registers, token rows through LDS) for
+    bf16 / MX / a8w8 and the LDS-staged fallback for f32; 0 is the automatic
+    choice."""
     cfg = SMALL[name]
     if mode == "pseudo" and cfg.fmt == "a8w8" and cfg.I_s > cfg.I:
         pytest.skip("per-row fp8 intermediate needs a single pseudo chunk")
