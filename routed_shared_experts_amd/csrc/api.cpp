@@ -51,6 +51,10 @@ bool overlaps(const void* a, const void* b, size_t n) {
   return x < y + n && y < x + n;
 }
 
+// batches up to this many tokens use the self-sorting one-wave kernels when
+// their blocks have 16 rows
+constexpr int kSelfSortMaxTokens = 64;
+
 int auto_block_m(double rows_per_expert) {
   if (rows_per_expert <= 16) return 16;
   if (rows_per_expert <= 48) return 32;
@@ -63,6 +67,9 @@ struct Plan {
   int mode;  // resolved shared mode: NONE, PSEUDO or AUX
   int m;     // pseudo experts
   int k_total, E_total, block_m, capacity, max_blocks;
+  // self_sort: the one-wave GEMM kernels find each 16-row block's pairs in the
+  // routing ids themselves (block b = sb * E_total + e), so no sort launch runs
+  int self_sort, ss_blocks, h_rows;
   int dense_bm, dense_blocks;
   size_t off_ids, off_w, off_gamma, off_xq, off_xs, off_counts, off_offsets, off_nblk, off_sorted, off_sortws,
       off_bexp, off_h, off_hs, off_hsh, off_hshs, off_amax_sh, off_acc, off_pair, off_cnt, off_amax, off_end;
@@ -152,6 +159,15 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.block_m = a->block_m ? a->block_m : auto_block_m((double)P / pl.E_total);
   pl.capacity = moe_sort_capacity(a->T, pl.k_total, pl.E_total, pl.block_m);
   pl.max_blocks = pl.capacity / pl.block_m;
+  {
+    // the one-wave kernels must take both stages (32-bit buffer offsets)
+    const size_t ss_rows = (size_t)pl.E_total * ((a->T + 15) / 16) * 16;
+    const size_t hsz = fmt == FMT_A8W8 ? 2 : (size_t)h_elem_bytes(fmt);
+    pl.self_sort = pl.block_m == 16 && a->T <= kSelfSortMaxTokens && a->I % 32 == 0 && a->I_s % 32 == 0 &&
+                   ss_rows * a->I * hsz < 0x7FFFFFFFu;
+  }
+  pl.ss_blocks = pl.self_sort ? pl.E_total * ((a->T + 15) / 16) : 0;
+  pl.h_rows = pl.capacity > pl.ss_blocks * 16 ? pl.capacity : pl.ss_blocks * 16;
   pl.dense_bm = a->block_m ? a->block_m : auto_block_m((double)a->T);
   pl.dense_blocks = (a->T + pl.dense_bm - 1) / pl.dense_bm;
   const int esz_h = h_elem_bytes(fmt);
@@ -168,8 +184,8 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_sorted = take((size_t)pl.capacity * 4);
   pl.off_sortws = take(sort_scratch_bytes((int)P, pl.E_total));
   pl.off_bexp = take((size_t)pl.max_blocks * 4);
-  pl.off_h = take((size_t)pl.capacity * a->I * esz_h);
-  pl.off_hs = take(fmt == FMT_MX ? (size_t)pl.capacity * (a->I / 32) : 0);
+  pl.off_h = take((size_t)pl.h_rows * a->I * esz_h);
+  pl.off_hs = take(fmt == FMT_MX ? (size_t)pl.h_rows * (a->I / 32) : 0);
   const size_t dense_rows = (size_t)pl.dense_blocks * pl.dense_bm;
   const bool aux = pl.mode == MOE_SHARED_AUX;
   pl.off_hsh = take(aux ? dense_rows * a->I_s * esz_h : 0);
@@ -181,7 +197,7 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_pair = take((size_t)P * a->H * 4);
   // cleared by the sort launch: arrival counters, then the routed row amax (A8W8)
   pl.off_cnt = take(moe_stage2_counters(a->T, a->H) * 4);
-  pl.off_amax = take(fmt == FMT_A8W8 ? (size_t)pl.capacity * 4 : 0);
+  pl.off_amax = take(fmt == FMT_A8W8 ? (size_t)pl.h_rows * 4 : 0);
   pl.off_end = o;
   pl.zero_begin = pl.off_cnt;
   pl.zero_end = o;
@@ -544,6 +560,26 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   rp.xq = fmt == FMT_MX ? xq : nullptr;
   rp.xs = fmt == FMT_MX ? xs : nullptr;
   rp.do_route = 1;
+
+  // sort (+ clearing of the accumulator unless the addend fills it)
+  SortParams sp{};
+  sp.ids = ids;
+  sp.P = a->T * pl.k_total;
+  sp.n_experts = pl.E_total;
+  sp.block_m = pl.block_m;
+  sp.capacity = pl.capacity;
+  sp.sorted = sorted;
+  sp.block_expert = bexp;
+  sp.counts = counts;
+  sp.offsets = offsets;
+  sp.num_blocks = nblk;
+  sp.chunk_base = sort_scratch_bytes(sp.P, pl.E_total) ? reinterpret_cast<int32_t*>(ws + pl.off_sortws) : nullptr;
+  sp.zero_ptr = reinterpret_cast<uint4*>(ws + pl.zero_begin);
+  sp.zero_vec = (long long)((pl.zero_end - pl.zero_begin) / 16);
+  if (pl.self_sort) {  // no sort launch: the routing launch clears the region
+    rp.zero_ptr = sp.zero_ptr;
+    rp.zero_vec = sp.zero_vec;
+  }
   HIP_TRY(launch_route(rp, main_s));
   if (tev) HIP_TRY(hipEventRecord(tev[1], main_s));
 
@@ -588,28 +624,16 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
     HIP_TRY(hipEventRecord(ev_ready, aux_s));
   }
 
-  // 3. sort (+ clearing of the accumulator unless the addend fills it)
-  SortParams sp{};
-  sp.ids = ids;
-  sp.P = a->T * pl.k_total;
-  sp.n_experts = pl.E_total;
-  sp.block_m = pl.block_m;
-  sp.capacity = pl.capacity;
-  sp.sorted = sorted;
-  sp.block_expert = bexp;
-  sp.counts = counts;
-  sp.offsets = offsets;
-  sp.num_blocks = nblk;
-  sp.chunk_base = sort_scratch_bytes(sp.P, pl.E_total) ? reinterpret_cast<int32_t*>(ws + pl.off_sortws) : nullptr;
-  sp.zero_ptr = reinterpret_cast<uint4*>(ws + pl.zero_begin);
-  sp.zero_vec = (long long)((pl.zero_end - pl.zero_begin) / 16);
-  HIP_TRY(launch_sort(sp, main_s));
+  // 3. sort (self-sorted blocks need none)
+  if (!pl.self_sort) HIP_TRY(launch_sort(sp, main_s));
   if (tev) HIP_TRY(hipEventRecord(tev[2], main_s));
 
   // 4. routed stage 1
   g.dense = 0;
   g.block_m = pl.block_m;
-  g.max_blocks = pl.max_blocks;
+  g.max_blocks = pl.self_sort ? pl.ss_blocks : pl.max_blocks;
+  g.self_sort = pl.self_sort;
+  g.ids = ids;
   g.sorted = sorted;
   g.block_expert = bexp;
   g.num_blocks = nblk;

@@ -347,6 +347,7 @@ hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStrea
   // 16-row blocks: weights and activations streamed straight into registers,
   // one wave per 32 (stage 1) or 64 (stage 2) columns of a block
   if (p.block_m == 16 && wave_kernel_fits(p, stage, fmt)) return launch_gemm_wave(p, stage, fmt, s);
+  if (p.self_sort) return hipErrorInvalidValue;  // only the one-wave kernels scan the ids
   // 32-128-row blocks: weights streamed into registers, token rows through LDS
   if (tile_kernel_fits(p, stage, fmt)) return launch_gemm_tile(p, stage, fmt, s);
   return stage == 1 ? launch_stage<1>(p, fmt, bn, s) : launch_stage<2>(p, fmt, bn, s);

@@ -153,6 +153,10 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);  // bf16 h quantised while staged
   constexpr int XG = kQuantA ? 2 : 1;                        // 16-byte global loads per staged chunk
   constexpr int CPT = NB / 2;                                // staged 16-byte chunks per thread per K tile
+  // bf16 runs on 32x32x16 MFMA tiles (the 16x16x32 form issues at half the
+  // rate on gfx950); the fp8 formats on the block-scaled 16x16x128 form
+  constexpr bool k32 = (FMT == FMT_BF16);
+  constexpr int NN = NB / 2;  // 32-row token groups of a block (k32)
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -177,12 +181,21 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    // stage 1: gate rows c0.., c0+16.. then the same up rows
-    const int rb = (STAGE == 1) ? c0 / 16 + (mb & 1) : c0 / 16 + mb;
+    // 16-row blocks (stage 1: gate rows c0.., c0+16.. then the same up rows);
+    // k32: 32-row blocks, stage 1 gate rows c0.. and up rows c0.., stage 2
+    // rows c0.. and c0+32..
+    int rb = (STAGE == 1) ? c0 / 16 + (mb & 1) : c0 / 16 + mb;
+    if (k32) rb = (STAGE == 1) ? c0 / 16 : c0 / 16 + 2 * (mb & 1);
     wtile[mb] = (uint32_t)tile_off(ev, rb, 0);
     stile[mb] = (uint32_t)scale_tile_off(ev, rb, 0);
   }
-  const uint32_t wlane = (uint32_t)lane * 16;
+  // 16x16 operands: lane (g, r) reads chunk position lane of each 1 KiB half.
+  // k32: lane l takes row l % 32 (tile row block (l % 32) / 16, row l % 16)
+  // and, at K step s of 16 elements, the 16-byte chunk 2s + l / 32 of the
+  // 128-byte K tile, which sits at 512 s + 16 (16 (l / 32) + l % 16) in the
+  // tile: two contiguous 512-byte runs per row block and step.
+  const uint32_t kfrag32 = (uint32_t)(((lane / 32) * 16 + l16) * 16);
+  const uint32_t wlane = k32 ? (uint32_t)(((lane % 32) / 16) * ev.nkt * 2048) + kfrag32 : (uint32_t)lane * 16;
 
   // ---- staged token rows: chunk q = tid + 256 u is (row block q/128, half,
   // lane group, row) in operand order; padding rows read past the buffer ----
@@ -216,6 +229,18 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   auto load_w = [&](uint4 (&w)[4][2], int (&sc)[4], int kt) {
     kt = kt < nk ? kt : nk - 1;  // past the end: a harmless reload of the last tile
+    if constexpr (k32) {
+      // w[2 mm + s / 2][s % 2]: M block mm, K step s
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const __amdgpu_buffer_rsrc_t r = wrs[(STAGE == 1) ? mm : 0];
+        const uint32_t so = wtile[mm] + (uint32_t)kt * 2048;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) w[2 * mm + st / 2][st % 2] = tile_load16(r, wlane + 512 * st, so);
+        sc[2 * mm] = sc[2 * mm + 1] = 127;
+      }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const __amdgpu_buffer_rsrc_t r = wrs[mb >> 1];
@@ -229,27 +254,30 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     }
   };
 
-  uint4 xr[CPT][XG];
-  uint32_t xsr = 0;
-  auto load_x = [&](int kt) {
+  // token-row register sets in flight: XD = 2 keeps the rows of K tiles
+  // kt + 1 and kt + 2 loading while tile kt is multiplied
+  constexpr int XD = (kQuantA || (FMT == FMT_A8W8 && NB == 8)) ? 1 : 2;
+  uint4 xr[XD][CPT][XG];
+  uint32_t xsr[XD] = {};
+  auto load_x = [&](int set, int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
 #pragma unroll
-      for (int h = 0; h < XG; ++h) xr[u][h] = tile_load16(xrs, xoff[u] + h * 16, (uint32_t)kt * 128 * XG);
+      for (int h = 0; h < XG; ++h) xr[set][u][h] = tile_load16(xrs, xoff[u] + h * 16, (uint32_t)kt * 128 * XG);
     if constexpr (FMT == FMT_MX) {
-      if (tid < BM) xsr = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);
+      if (tid < BM) xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);
     }
   };
-  auto store_x = [&](int buf) {
+  auto store_x = [&](int buf, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int q = tid + kTileThreads * u;
       uint4 v;
       if constexpr (kQuantA) {
         const float inv = sm.inv[(q / 128) * 16 + (q % 16)];
-        const uint32_t w[8] = {xr[u][0].x, xr[u][0].y, xr[u][0].z, xr[u][0].w,
-                               xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w};
+        const uint32_t w[8] = {xr[set][u][0].x, xr[set][u][0].y, xr[set][u][0].z, xr[set][u][0].w,
+                               xr[set][u][1].x, xr[set][u][1].y, xr[set][u][1].z, xr[set][u][1].w};
         uint32_t o[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -257,23 +285,46 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
                             bf16_to_f32(w[2 * t + 1] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t + 1] >> 16) * inv);
         v = make_uint4(o[0], o[1], o[2], o[3]);
       } else {
-        v = xr[u][0];
+        v = xr[set][u][0];
       }
       *reinterpret_cast<uint4*>(&sm.x[buf][q * 16]) = v;
     }
     if constexpr (FMT == FMT_MX) {
-      if (tid < BM) sm.xsc[buf][tid] = xsr;
+      if (tid < BM) sm.xsc[buf][tid] = xsr[set];
     }
   };
 
+  // one of the two accumulator sets is used (the other is dead code)
   f32x4 acc[4][NB];
+  f32x16 acc32[2][NN];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc32[mm][nn][v] = 0.f;
+  // k32 token fragment of lane l: row block (l % 32) / 16 of a 32-row group
+  const uint32_t xfrag32 = (uint32_t)(((lane % 32) / 16) * 2048) + kfrag32;
 
   auto compute = [&](int buf, const uint4 (&w)[4][2], const int (&sc)[4]) {
-    if constexpr (FMT == FMT_BF16) {
+    if constexpr (k32) {
+      // four K steps of 16; consecutive MFMAs update different accumulators
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) {
+          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32 + 512 * st]);
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+            acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf), acc32[mm][nn],
+                0, 0, 0);
+        }
+    } else if constexpr (FMT == FMT_BF16) {
       // two K=32 halves; the half is the outer loop so that consecutive MFMAs
       // update different accumulators
 #pragma unroll
@@ -301,26 +352,43 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   // Two weight register sets and two LDS buffers in ping-pong: while K tile
   // kt is multiplied, the weights of kt + 1 are in flight (issued one step
-  // earlier) and the token rows of kt + 1 are loaded and then staged.  Every
-  // step is unconditional; loads past the end reload the last tile.
+  // earlier) and the token rows of kt + 1 (XD = 1) or of kt + 1 and kt + 2
+  // (XD = 2, register set = tile parity) are loading; after the multiply the
+  // rows of kt + 1 are staged into the other LDS buffer.  Every step is
+  // unconditional; loads past the end reload the last tile.
+  // The prologue issues its loads in the order the loop keeps in flight
+  // (rows kt + 1, weights kt, rows kt + 2, weights kt + 1): the wait counts
+  // the compiler derives at the loop head hold for the first pass too, so
+  // staging a tile never waits for loads issued after it.
   uint4 wA[4][2], wB[4][2];
   int sA[4], sB[4];
-  load_w(wA, sA, 0);
-  load_w(wB, sB, 1);
-  load_x(0);
-  store_x(0);
+  if constexpr (XD == 2) {
+    load_x(0, 0);
+    load_x(1, 1);
+    load_w(wA, sA, 0);
+    store_x(0, 0);
+    load_x(0, 2);
+    load_w(wB, sB, 1);
+  } else {
+    load_w(wA, sA, 0);
+    load_w(wB, sB, 1);
+    load_x(0, 0);
+    store_x(0, 0);
+  }
   __syncthreads();
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
-    load_x(kt + 1);
+    if constexpr (XD == 1) load_x(0, kt + 1);
     compute(0, wA, sA);
     load_w(wA, sA, kt + 2);
-    store_x(1);
+    store_x(1, XD - 1);
+    if constexpr (XD == 2) load_x(1, kt + 3);
     __syncthreads();
-    load_x(kt + 2);
+    if constexpr (XD == 1) load_x(0, kt + 2);
     compute(1, wB, sB);
     load_w(wB, sB, kt + 3);
-    store_x(0);
+    store_x(0, 0);
+    if constexpr (XD == 2) load_x(0, kt + 4);
     __syncthreads();
   }
   if (kt < nk) compute(0, wA, sA);  // odd tile count: the last tile sits in buffer 0 / set A
@@ -328,7 +396,26 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // ---- epilogues (per wave, from registers) ----
   // acc[mb][nb][v] = row (mb, 4g + v) of the wave's weight rows x token row nb*16 + l16
   if (!wave_ok) return;
-  if constexpr (STAGE == 1) {
+  // k32: acc32[mm][nn][4 j + v] = weight row 8 j + 4 (l / 32) + v of M block
+  // mm x token row nn * 32 + l % 32
+  if constexpr (STAGE == 1 && k32) {
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const int r = nn * 32 + lane % 32;
+      if (sm.tok[r] < 0) continue;
+      const size_t slot = (size_t)b * BM + r;
+      const float sc = sm.rs[r] * ev.wscale;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.h) + slot * p.ld_h + c0 + 4 * (lane / 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t bits[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          bits[v] = f32_to_bf16(silu_mul(acc32[0][nn][4 * j + v] * sc, acc32[1][nn][4 * j + v] * sc));
+        *reinterpret_cast<uint2*>(dst + 8 * j) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+      }
+    }
+  } else if constexpr (STAGE == 1) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int r = nb * 16 + l16;
@@ -390,6 +477,25 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       }
     }
   } else {
+    if (p.mode == 0 && k32) {  // STORE: gamma * S(x), the dense shared expert's addend
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) {
+        const int r = nn * 32 + lane % 32;
+        const int tok = sm.tok[r];
+        if (tok < 0) continue;
+        const float sc = sm.rs[r] * ev.wscale;
+        const float gm = p.gamma ? p.gamma[tok] : 1.0f;
+        float* dst = p.acc + (size_t)tok * p.H + c0 + 4 * (lane / 32);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(dst + 32 * mm + 8 * j) =
+                make_float4(gm * (acc32[mm][nn][4 * j] * sc), gm * (acc32[mm][nn][4 * j + 1] * sc),
+                            gm * (acc32[mm][nn][4 * j + 2] * sc), gm * (acc32[mm][nn][4 * j + 3] * sc));
+      }
+      return;
+    }
     if (p.mode == 0) {  // STORE: gamma * S(x), the dense shared expert's addend
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -408,19 +514,38 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     }
     // ACCUMULATE: the weighted pair rows (64 columns each); the tile's
     // reduction is XCD-local, so ordinary stores
+    if constexpr (k32) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int r = nb * 16 + l16;
-      const int pair = sm.pair[r];
-      if (pair < 0) continue;
-      const float sc = sm.rs[r] * ev.wscale;
-      const float wgt = sm.rw[r];
-      float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * g;
+      for (int nn = 0; nn < NN; ++nn) {
+        const int r = nn * 32 + lane % 32;
+        const int pair = sm.pair[r];
+        if (pair < 0) continue;
+        const float sc = sm.rs[r] * ev.wscale;
+        const float wgt = sm.rw[r];
+        float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * (lane / 32);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        *reinterpret_cast<float4*>(dst + mb * 16) =
-            make_float4(wgt * (acc[mb][nb][0] * sc), wgt * (acc[mb][nb][1] * sc), wgt * (acc[mb][nb][2] * sc),
-                        wgt * (acc[mb][nb][3] * sc));
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(dst + 32 * mm + 8 * j) =
+                make_float4(wgt * (acc32[mm][nn][4 * j] * sc), wgt * (acc32[mm][nn][4 * j + 1] * sc),
+                            wgt * (acc32[mm][nn][4 * j + 2] * sc), wgt * (acc32[mm][nn][4 * j + 3] * sc));
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + l16;
+        const int pair = sm.pair[r];
+        if (pair < 0) continue;
+        const float sc = sm.rs[r] * ev.wscale;
+        const float wgt = sm.rw[r];
+        float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          *reinterpret_cast<float4*>(dst + mb * 16) =
+              make_float4(wgt * (acc[mb][nb][0] * sc), wgt * (acc[mb][nb][1] * sc), wgt * (acc[mb][nb][2] * sc),
+                          wgt * (acc[mb][nb][3] * sc));
+      }
     }
     // count arrivals once the stores have reached the L2 (their acknowledgement);
     // all of the block's counter atomics are issued before any result is used
@@ -428,29 +553,42 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     __builtin_amdgcn_s_waitcnt(0);
     const int n_tiles = p.H / 64;
     const int tile = c0 / 64;
-    int old[NB];
+    // cnt[nb]: 16-bit mask of the done (last-arrival) tokens of row block nb
+    uint32_t cnt[NB];
+    int total = 0;
+    if constexpr (k32) {
+      // lanes 0..31 hold the 32 tokens of each group
+      int old[NN];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int r = nb * 16 + l16;
-      old[nb] = -1;
-      if (g == 0 && sm.pair[r] >= 0) old[nb] = atomicAdd(p.counters + (size_t)sm.tok[r] * n_tiles + tile, 1);
+      for (int nn = 0; nn < NN; ++nn) {
+        const int r = nn * 32 + lane % 32;
+        old[nn] = -1;
+        if (lane < 32 && sm.pair[r] >= 0) old[nn] = atomicAdd(p.counters + (size_t)sm.tok[r] * n_tiles + tile, 1);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) {
+        const uint64_t m = __ballot(old[nn] == p.expected - 1);  // only lanes < 32 can match
+        cnt[2 * nn] = (uint32_t)m & 0xFFFFu;
+        cnt[2 * nn + 1] = (uint32_t)(m >> 16) & 0xFFFFu;
+      }
+    } else {
+      int old[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + l16;
+        old[nb] = -1;
+        if (g == 0 && sm.pair[r] >= 0) old[nb] = atomicAdd(p.counters + (size_t)sm.tok[r] * n_tiles + tile, 1);
+      }
+      // lanes 0..15 hold the tokens of each row block
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) cnt[nb] = (uint32_t)__ballot(old[nb] == p.expected - 1 && g == 0) & 0xFFFFu;
     }
-    // done bits of the block's (row block, token) slots, spread to the token's four lanes
-    uint32_t done = 0;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) done |= (uint32_t)(__shfl(old[nb], l16, kWave) == p.expected - 1) << nb;
+    for (int nb = 0; nb < NB; ++nb) total += __popc(cnt[nb]);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // the wave's last arrivals, compacted 16 at a time: entry i -> lanes
     // (g, i % 16), each summing 16 of the tile's 64 columns
-    if (__ballot(done != 0)) {
-      uint32_t cnt[NB];
-      int total = 0;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // 16-bit mask of the row block's done tokens (lanes 0..15 hold them)
-        cnt[nb] = (uint32_t)__ballot(((done >> nb) & 1u) != 0 && g == 0) & 0xFFFFu;
-        total += __popc(cnt[nb]);
-      }
+    if (total > 0) {
       for (int base = 0; base < total; base += 16) {
         const int i = base + l16;
         if (i < total) {

@@ -59,13 +59,18 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   const int ncw = width_max / CW;
   const int b = blockIdx.x / ncw, c0 = (blockIdx.x % ncw) * CW;
 
-  // block expert and this lane's token, fetched together
+  // block expert and this lane's token (sorted blocks: fetched together)
   const int slot_l = b * BM + l16;
-  int e, pair_l = -1, tok_l;
+  int e, sb = 0, pair_l = -1, tok_l = -1;
   if (p.dense) {
     if (b * BM >= p.T) return;
     e = -1;
     tok_l = slot_l < p.T ? slot_l : -1;
+  } else if (p.self_sort) {
+    // block b = sb * E' + e holds expert e's pairs of rank 16 sb .. 16 sb + 15
+    const int Et = p.E + p.n_pseudo;
+    e = b % Et;
+    sb = b / Et;
   } else {
     e = p.block_expert[b];  // -1 past the last block
     const int pr = p.sorted[slot_l];
@@ -87,6 +92,68 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   if constexpr (NW == 2) {
     wbase[1] = ev.wb + lane * 16;
     sbase[1] = ev.sb + lane;
+  }
+  // row block of group cgi (rows past a narrow chunk read row block 0 and are
+  // never stored)
+  auto group_rb = [&](int cgi) {
+    const int r0 = c0 + cgi * 16;
+    return (STAGE == 1 && r0 >= ev.width) ? 0 : r0 / 16;
+  };
+  // K tile outermost: one activation tile feeds every group of the wave;
+  // D K tiles of all NCG * NW weight tiles in flight
+  uint4 wb[D][NCG][NW][2];
+  int wsc[D][NCG][NW];
+  auto load_w = [&](int d, int kt) {
+    kt = kt < nk ? kt : nk - 1;  // unconditional loads: no branch forces a full wait
+#pragma unroll
+    for (int cgi = 0; cgi < NCG; ++cgi) {
+      const int rb = group_rb(cgi);
+      const size_t off = tile_off(ev, rb, kt);
+#pragma unroll
+      for (int m = 0; m < NW; ++m) {
+        wb[d][cgi][m][0] = ld16(wbase[m] + off);
+        wb[d][cgi][m][1] = ld16(wbase[m] + off + 1024);
+        if constexpr (FMT == FMT_MX) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
+        else wsc[d][cgi][m] = 127;
+      }
+    }
+  };
+  // Self-sorted blocks: the first block of an expert is almost always
+  // occupied, so its weights start streaming before the token scan; later
+  // blocks scan first (most of them are empty and leave).
+  const bool early_w = p.self_sort && sb == 0;
+  if (early_w) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(d, d);
+  }
+  if (!p.dense && p.self_sort) {
+    // the block's pairs: ranks 16 sb .. 16 sb + 15 of expert e among the
+    // T * k_total ids in pair order (ascending pair index, as the sort orders them)
+    __shared__ int s_pair[BM];
+    const int P = p.T * p.k_total;
+    int cum = 0;
+    for (int base = 0; base < P; base += 4 * kWave) {
+      int idv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kWave + lane;
+        idv[u] = i < P ? p.ids[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool hit = idv[u] == e;
+        const uint64_t m = __ballot(hit);
+        const int r = cum - BM * sb +
+                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (hit && r >= 0 && r < BM) s_pair[r] = base + u * kWave + lane;
+        cum += (int)__popcll(m);
+      }
+    }
+    const int rows = cum - BM * sb;
+    if (rows <= 0) return;
+    wave_lds_sync();
+    pair_l = l16 < rows ? s_pair[l16] : -1;
+    tok_l = pair_l >= 0 ? pair_l / p.k_total : -1;
   }
   // ---- activations: this lane's token row through a buffer descriptor ----
   const bool xok = tok_l >= 0;
@@ -161,39 +228,19 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
       x1 = xb[d][1];
     }
   };
-  // row block of group cgi (rows past a narrow chunk read row block 0 and are
-  // never stored)
-  auto group_rb = [&](int cgi) {
-    const int r0 = c0 + cgi * 16;
-    return (STAGE == 1 && r0 >= ev.width) ? 0 : r0 / 16;
-  };
-
   // lane results: rows 4g..4g+3 of each group (columns c0 + 16 cgi + 4g + j),
   // token l16
   const float sc = rs * ev.wscale;
   float res[NCG][4];
-  // K tile outermost: one activation tile feeds every group of the wave;
-  // D K tiles of all NCG * NW weight tiles in flight
-  uint4 wb[D][NCG][NW][2];
-  int wsc[D][NCG][NW];
   auto load = [&](int d, int kt) {
-    kt = kt < nk ? kt : nk - 1;  // unconditional loads: no branch forces a full wait
-#pragma unroll
-    for (int cgi = 0; cgi < NCG; ++cgi) {
-      const int rb = group_rb(cgi);
-      const size_t off = tile_off(ev, rb, kt);
-#pragma unroll
-      for (int m = 0; m < NW; ++m) {
-        wb[d][cgi][m][0] = ld16(wbase[m] + off);
-        wb[d][cgi][m][1] = ld16(wbase[m] + off + 1024);
-        if constexpr (FMT == FMT_MX) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
-        else wsc[d][cgi][m] = 127;
-      }
-    }
-    load_x(d, kt);
+    load_w(d, kt);
+    load_x(d, kt < nk ? kt : nk - 1);
   };
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(d, d);
+  for (int d = 0; d < D; ++d) {
+    if (!early_w) load_w(d, d);
+    load_x(d, d);
+  }
   f32x4 acc[NCG][NW];
 #pragma unroll
   for (int cgi = 0; cgi < NCG; ++cgi)

@@ -28,6 +28,9 @@ struct RouteParams {
   uint8_t* xq;
   uint8_t* xs;
   int do_route;
+  // region cleared by the workgroups after the routing ones (or NULL)
+  uint4* zero_ptr;
+  long long zero_vec;
 };
 
 struct SortParams {
@@ -56,6 +59,11 @@ struct GemmParams {
   const uint8_t* x;
   const void* x_s;
   int dense, block_m, max_blocks;
+  // self_sort (16-row blocks of the one-wave kernel): block b = sb * (E + n_pseudo)
+  // + e holds expert e's pairs of rank 16 sb.. in pair order, found by scanning
+  // ids [T][k_total]; sorted / block_expert / num_blocks are then unused
+  int self_sort;
+  const int32_t* ids;
   const int32_t* sorted;
   const int32_t* block_expert;
   const int32_t* num_blocks;

@@ -2,129 +2,23 @@
 // commit 2, and the review's "moe_sorting without zeroing" experiment: the
 // sort also clears the output accumulator unless an addend is present).
 //
-// Workgroup 0 (1024 threads) does the whole sort in LDS:
-//   1. histogram of expert ids (LDS atomics; counts are order-independent);
-//   2. exclusive scan of the counts padded to block_m, block -> expert map;
-//   3. a stable scatter: pairs are taken in index order, 1024 per round; the
-//      rank of a pair among equal experts of its wave comes from a ballot
-//      match on the expert id bits, and the wave's base from the per-wave
-//      counts of the waves before it, so the output order is ascending pair
-//      index inside each expert independently of scheduling.
-// Workgroups 1.. clear the requested region with 16-byte stores.
+// Workgroup 0 (1024 threads) does the whole sort in LDS (sort_wg in
+// prologue.hpp: histogram, padded scan and block map, stable ballot-ranked
+// scatter); workgroups 1.. clear the requested region with 16-byte stores.
 // Larger pair counts use the three-launch variant further below.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "prologue.hpp"
 
 namespace moe {
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kMaxSortExperts = 576;
 constexpr int kSmallSort = 8192;  // pair counts up to this use the single-workgroup sort
 
 __global__ __launch_bounds__(kSortThreads) void sort_kernel(SortParams p) {
   if (blockIdx.x > 0) {
-    const long long stride = (long long)(gridDim.x - 1) * kSortThreads;
-    for (long long i = (long long)(blockIdx.x - 1) * kSortThreads + threadIdx.x; i < p.zero_vec; i += stride)
-      p.zero_ptr[i] = make_uint4(0, 0, 0, 0);
+    clear_region(p.zero_ptr, p.zero_vec, 1);
     return;
   }
-  __shared__ int s_count[kMaxSortExperts];
-  __shared__ int s_off[kMaxSortExperts + 1];
-  __shared__ int s_run[kMaxSortExperts];
-  __shared__ int s_wave[kSortWaves][kMaxSortExperts];
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wv = tid / kWave;
-  const int nE = p.n_experts;
-  const int BM = p.block_m;
-
-  for (int e = tid; e < nE; e += kSortThreads) {
-    s_count[e] = 0;
-    s_run[e] = 0;
-  }
-  for (int i = tid; i < kSortWaves * kMaxSortExperts; i += kSortThreads) (&s_wave[0][0])[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < p.P; i += kSortThreads) atomicAdd(&s_count[p.ids[i]], 1);
-  __syncthreads();
-
-  // padded exclusive scan by wave 0, 64 experts at a time
-  if (wv == 0) {
-    int carry = 0;
-    for (int base = 0; base < nE; base += kWave) {
-      int e = base + lane;
-      int c = e < nE ? s_count[e] : 0;
-      int pc = (c + BM - 1) / BM * BM;
-      int incl = pc;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-      }
-      if (e < nE) s_off[e] = carry + incl - pc;
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (lane == 0) s_off[nE] = carry;
-  }
-  __syncthreads();
-  const int total = s_off[nE];
-  const int nblk = total / BM;
-  for (int e = tid; e < nE; e += kSortThreads) {
-    p.counts[e] = s_count[e];
-    p.offsets[e] = s_off[e];
-  }
-  if (tid == 0) {
-    p.offsets[nE] = total;
-    *p.num_blocks = nblk;
-  }
-  // block -> expert (upper bound search over the padded offsets)
-  const int max_blocks = p.capacity / BM;
-  for (int b = tid; b < max_blocks; b += kSortThreads) {
-    int be = -1;
-    if (b < nblk) {
-      int row = b * BM, lo = 0, hi = nE - 1;
-      while (lo < hi) {  // last e with s_off[e] <= row
-        int mid = (lo + hi + 1) / 2;
-        if (s_off[mid] <= row) lo = mid; else hi = mid - 1;
-      }
-      be = lo;
-    }
-    p.block_expert[b] = be;
-  }
-  // sentinels: padding slots of each expert, and the unused tail
-  for (int e = tid; e < nE; e += kSortThreads)
-    for (int i = s_off[e] + s_count[e]; i < s_off[e + 1]; ++i) p.sorted[i] = p.P;
-  for (int i = total + tid; i < p.capacity; i += kSortThreads) p.sorted[i] = p.P;
-
-  // stable scatter
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < p.P; base += kSortThreads) {
-    const int pi = base + tid;
-    const bool valid = pi < p.P;
-    const int e = valid ? p.ids[pi] : 0;
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const bool b = (e >> bit) & 1;
-      const uint64_t bal = __ballot(b);
-      peers &= b ? bal : ~bal;
-    }
-    const int rank = __popcll(peers & lt_mask);
-    const int leader = valid ? (__ffsll((unsigned long long)peers) - 1) : -1;
-    if (valid && lane == leader) s_wave[wv][e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int pos = s_off[e] + s_run[e] + rank;
-      for (int w = 0; w < wv; ++w) pos += s_wave[w][e];
-      p.sorted[pos] = pi;
-    }
-    __syncthreads();
-    if (valid && lane == leader) {
-      atomicAdd(&s_run[e], s_wave[wv][e]);
-      s_wave[wv][e] = 0;
-    }
-    __syncthreads();
-  }
+  __shared__ SortSmem sm;
+  sort_wg(p, p.ids, sm);
 }
 
 // ---- three-launch sort for large pair counts --------------------------------
@@ -139,9 +33,7 @@ constexpr int kChunk = kSortThreads;  // pairs per chunk (one per thread)
 __global__ __launch_bounds__(kSortThreads) void sort_count_kernel(SortParams p) {
   const int nchunk = (p.P + kChunk - 1) / kChunk;
   if ((int)blockIdx.x >= nchunk) {
-    const long long stride = (long long)(gridDim.x - nchunk) * kSortThreads;
-    for (long long i = (long long)(blockIdx.x - nchunk) * kSortThreads + threadIdx.x; i < p.zero_vec; i += stride)
-      p.zero_ptr[i] = make_uint4(0, 0, 0, 0);
+    clear_region(p.zero_ptr, p.zero_vec, nchunk);
     return;
   }
   __shared__ int s_count[kMaxSortExperts];
@@ -251,11 +143,7 @@ size_t sort_scratch_bytes(int P, int n_experts) {
 }
 
 hipError_t launch_sort(const SortParams& p, hipStream_t s) {
-  long long zblocks = 0;
-  if (p.zero_vec > 0) {
-    zblocks = (p.zero_vec + kSortThreads * 4 - 1) / (kSortThreads * 4);
-    if (zblocks > 1024) zblocks = 1024;
-  }
+  const long long zblocks = clear_blocks(p.zero_vec, kSortThreads);
   if (p.chunk_base == nullptr || p.P <= kSmallSort) {
     hipLaunchKernelGGL(sort_kernel, dim3(1 + (int)zblocks), dim3(kSortThreads), 0, s, p);
     return hipGetLastError();
