@@ -637,6 +637,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.sorted = sorted;
   g.block_expert = bexp;
   g.num_blocks = nblk;
+  g.offsets = pl.self_sort ? nullptr : offsets;
   g.h = ws + pl.off_h;
   g.ld_h = a->I;
   g.h_s = fmt == FMT_MX ? static_cast<void*>(ws + pl.off_hs)

@@ -40,9 +40,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   constexpr int BROWS = (STAGE == 1) ? 2 * BN : BN;
   constexpr int A_CH = BM * 8, B_CH = BROWS * 8;
   constexpr int A_PER = (A_CH + 255) / 256, B_PER = (B_CH + 255) / 256;
-  // stage-2 A8W8 reads bf16 h and quantises it while staging into LDS
-  constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);
-  constexpr int A_GMUL = kQuantA ? 2 : 1;
   constexpr int TILE_BYTES = 2 * (BM + BROWS) * 128;
   constexpr int EPI_BYTES = BM * (BN + 4) * 4;
   constexpr int SMEM = TILE_BYTES > EPI_BYTES ? TILE_BYTES : EPI_BYTES;
@@ -54,7 +51,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __shared__ int s_pair[BM];
   __shared__ float s_rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
   __shared__ float s_rw[BM];   // stage 2: pair weight / gate
-  __shared__ float s_inv[BM];  // stage 2 A8W8: 448 / amax
   __shared__ int s_done[BM];
 
   const int tid = threadIdx.x;
@@ -79,7 +75,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const ExpertView ev = resolve_expert<FMT, STAGE>(p, e);
   if (STAGE == 1 && n0 >= ev.width) return;  // tile past a narrow pseudo-expert chunk
 
-  setup_rows<FMT, STAGE, BM>(p, b, tid, s_tok, s_pair, s_rw, s_rs, s_inv);
+  setup_rows<FMT, STAGE, BM>(p, b, tid, s_tok, s_pair, s_rw, s_rs);
   __syncthreads();
 
   // ---- per-thread load descriptors ----
@@ -101,7 +97,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       } else {
         const int slot = b * BM + r;
         a_ok[q] = s_tok[r] >= 0;
-        a_ptr[q] = p.h + ((size_t)slot * p.ld_h * esz + c * 16) * A_GMUL;
+        a_ptr[q] = p.h + (size_t)slot * h_row_bytes<FMT>(p) + c * 16;
       }
     }
   }
@@ -130,7 +126,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     }
   }
 
-  uint4 ra[A_PER][A_GMUL];
+  uint4 ra[A_PER];
   uint4 rb[B_PER];
   uint32_t rasc = 0x7F7F7F7Fu, rbsc = 0x7F7F7F7Fu;
 
@@ -140,10 +136,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int q = 0; q < A_PER; ++q) {
       const int c = (tid + q * 256) % 8;
       const bool kin = (kb + c * 16) < kbytes;
-#pragma unroll
-      for (int u = 0; u < A_GMUL; ++u) {
-        ra[q][u] = (a_ok[q] && kin) ? ld16(a_ptr[q] + (size_t)kb * A_GMUL + u * 16) : make_uint4(0, 0, 0, 0);
-      }
+      ra[q] = (a_ok[q] && kin) ? ld16(a_ptr[q] + (size_t)kb) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
@@ -198,21 +191,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       const int cid = tid + q * 256;
       if (cid < A_CH) {
         const int r = cid / 8, c = cid % 8;
-        uint4 v;
-        if constexpr (kQuantA) {
-          const float inv = s_inv[r];
-          const uint32_t w[8] = {ra[q][0].x, ra[q][0].y, ra[q][0].z, ra[q][0].w,
-                                 ra[q][1].x, ra[q][1].y, ra[q][1].z, ra[q][1].w};
-          uint32_t o[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[u] = pack4_e4m3(bf16_to_f32(w[2 * u] & 0xFFFFu) * inv, bf16_to_f32(w[2 * u] >> 16) * inv,
-                              bf16_to_f32(w[2 * u + 1] & 0xFFFFu) * inv, bf16_to_f32(w[2 * u + 1] >> 16) * inv);
-          v = make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
-          v = ra[q][0];
-        }
-        *reinterpret_cast<uint4*>(sA + swz(r, c)) = v;
+        *reinterpret_cast<uint4*>(sA + swz(r, c)) = ra[q];
       }
     }
 #pragma unroll
@@ -343,7 +322,63 @@ static hipError_t launch_stage(const GemmParams& p, int fmt, int bn, hipStream_t
   }
 }
 
+// A8W8 stage-2 input (per-row rule: q = e4m3_rne_sat(v * 448 / amax) over the
+// bf16 values v of the row, amax their largest magnitude from stage 1): each
+// row of h is quantised once, in place -- its codes go to the first ld_h bytes
+// of the row's 2 ld_h-byte bf16 storage.  One wave per row, lane chunks of 8
+// values in increasing order, so the codes of chunk c (bytes 8c..8c+7) only
+// overwrite values of chunk c / 2, which the wave has already loaded.  Rows
+// with amax = 0 (padding, empty blocks, all-zero rows) are left as they are:
+// their bytes are zero or never read.
+__global__ __launch_bounds__(256) void quant_rows_kernel(uint8_t* h, const float* amax, int rows, int ld_h,
+                                                         const int32_t* num_blocks, int block_m) {
+  constexpr int U = 4;  // chunks of 8 values per lane per round
+  const int lane = threadIdx.x % kWave;
+  const int nrows = num_blocks ? min(rows, *num_blocks * block_m) : rows;
+  const int nchunk = ld_h / 8;
+  for (int r = blockIdx.x * 4 + (int)threadIdx.x / kWave; r < nrows; r += gridDim.x * 4) {
+    const float a = amax[r];
+    if (!(a > 0.f)) continue;
+    const float inv = __fdiv_rn(448.0f, a);
+    uint8_t* row = h + (size_t)r * ld_h * 2;
+    for (int base = 0; base < nchunk; base += U * kWave) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * kWave + lane;
+        v[u] = c < nchunk ? *reinterpret_cast<const uint4*>(row + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * kWave + lane;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t o[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          o[t] = pack4_e4m3(bf16_to_f32(w[2 * t] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t] >> 16) * inv,
+                            bf16_to_f32(w[2 * t + 1] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t + 1] >> 16) * inv);
+        if (c < nchunk) *reinterpret_cast<uint2*>(row + (size_t)c * 8) = make_uint2(o[0], o[1]);
+      }
+    }
+  }
+}
+
+hipError_t launch_quant_rows(const GemmParams& p, hipStream_t s) {
+  const int rows = p.max_blocks * p.block_m;
+  const int32_t* nblk = (p.dense || p.self_sort) ? nullptr : p.num_blocks;
+  int grid = (rows + 3) / 4;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(grid), dim3(256), 0, s, p.h, static_cast<const float*>(p.h_s), rows,
+                     p.ld_h, nblk, p.block_m);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStream_t s) {
+  if (stage == 2 && fmt == FMT_A8W8) {
+    const hipError_t e = launch_quant_rows(p, s);
+    if (e != hipSuccess) return e;
+  }
   // 16-row blocks: weights and activations streamed straight into registers,
   // one wave per 32 (stage 1) or 64 (stage 2) columns of a block
   if (p.block_m == 16 && wave_kernel_fits(p, stage, fmt)) return launch_gemm_wave(p, stage, fmt, s);

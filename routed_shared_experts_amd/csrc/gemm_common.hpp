@@ -25,6 +25,12 @@ struct FmtInfo<FMT_A8W8> { static constexpr int esz = 1; static constexpr bool f
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Non-temporal load for data read exactly once (decode weight streams): it
+// does not displace reusable lines from the caches.
+__device__ __forceinline__ uint4 ld16_stream(const uint8_t* p) {
+  const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
 
 template <int FMT>
 __device__ __forceinline__ void mfma_tile(f32x4& acc, const uint4& a0, const uint4& a1, const uint4& b0,
@@ -128,9 +134,17 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
 
 
 // Per-row description of a block of BM sorted slots (or dense tokens).
+// Bytes per row of the stage-2 input h: A8W8 rows keep the size of stage 1's
+// bf16 output and carry their e4m3 codes at the start (quantised in place by
+// quant_rows_kernel before stage 2).
+template <int FMT>
+__device__ __forceinline__ size_t h_row_bytes(const GemmParams& p) {
+  return (size_t)p.ld_h * (FMT == FMT_A8W8 ? 2 : FmtInfo<FMT>::esz);
+}
+
 template <int FMT, int STAGE, int BM>
 __device__ __forceinline__ void setup_rows(const GemmParams& p, int b, int tid, int* s_tok, int* s_pair,
-                                           float* s_rw, float* s_rs, float* s_inv) {
+                                           float* s_rw, float* s_rs) {
   const int P = p.T * p.k_total;
   if (tid < BM) {
     const int slot = b * BM + tid;
@@ -151,20 +165,16 @@ __device__ __forceinline__ void setup_rows(const GemmParams& p, int b, int tid, 
     s_tok[tid] = tok;
     s_pair[tid] = pair;
     s_rw[tid] = rw;
-    float rs = 1.0f, inv = 0.f;
+    float rs = 1.0f;
     if (FMT == FMT_A8W8) {
       if (STAGE == 1) {
         rs = tok >= 0 ? static_cast<const float*>(p.x_s)[tok] : 0.f;
       } else {
         const float amax = static_cast<const float*>(p.h_s)[slot];
-        if (amax > 0.f) {
-          inv = __fdiv_rn(448.0f, amax);
-          rs = __fdiv_rn(amax, 448.0f);
-        }
+        if (amax > 0.f) rs = __fdiv_rn(amax, 448.0f);
       }
     }
     s_rs[tid] = rs;
-    s_inv[tid] = inv;
   }
 }
 

@@ -28,8 +28,10 @@
 // reads from LDS, and 4 x NB MFMA tiles.
 //
 // Placement.  Workgroups are dealt round-robin to the eight XCDs.  Stage 1
-// remaps launch order so that consecutive logical tiles (the column tiles of
-// one block, then the next block of the same expert) share one XCD's L2.
+// remaps launch order so that consecutive logical tiles share one XCD's L2;
+// with the experts' row offsets at hand the logical order is expert-major
+// (the blocks of one weight column tile side by side), else block-major.  The
+// stage-2 queues below take the same expert-major order.
 // Stage 2 (ACCUMULATE) runs persistent workgroups that take work from one
 // queue per XCD: queue x holds the 64-column reduction tiles t = x (mod 8) of
 // every block, and a workgroup reads the XCD it actually runs on from the
@@ -69,6 +71,20 @@ __device__ __forceinline__ uint4 tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// Expert-major order of a launch's work: the items of expert e (its blocks x
+// n_per column tiles, a contiguous range in block-major order) are taken
+// column tile by column tile, the blocks of one column tile side by side, so
+// the concurrent workgroups of an expert share each weight tile through L2
+// instead of streaming the expert's weights once per block.  In: the item
+// index `it` of block-major order; out: block b and column tile c.
+__device__ __forceinline__ void expert_major(const GemmParams& p, int BM, int n_per, int it, int& b, int& c) {
+  const int e = p.block_expert[it / n_per];
+  const int bs = p.offsets[e] / BM, nb = (p.offsets[e + 1] - p.offsets[e]) / BM;
+  const int local = it - bs * n_per;
+  c = local / nb;
+  b = bs + local % nb;
+}
+
 template <int BM>
 struct TileSmem {
   uint8_t x[2][BM * 128];  // staged token rows, operand order
@@ -77,7 +93,6 @@ struct TileSmem {
   int pair[BM];
   float rw[BM];   // stage 2: pair weight / gate
   float rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
-  float inv[BM];  // stage 2 A8W8: 448 / amax
   int item;       // persistent stage 2: the claimed work item / queue
 };
 
@@ -150,8 +165,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
                                            int c0, bool wave_ok) {
   constexpr int esz = FmtInfo<FMT>::esz;
   constexpr int BM = 16 * NB;                                // sorted rows of a block
-  constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);  // bf16 h quantised while staged
-  constexpr int XG = kQuantA ? 2 : 1;                        // 16-byte global loads per staged chunk
   constexpr int CPT = NB / 2;                                // staged 16-byte chunks per thread per K tile
   // bf16 runs on 32x32x16 MFMA tiles (the 16x16x32 form issues at half the
   // rate on gfx950); the fp8 formats on the block-scaled 16x16x128 form
@@ -162,7 +175,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   const int lane = tid % kWave;
   const int g = lane / 16, l16 = lane % 16;
 
-  setup_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, sm.rw, sm.rs, sm.inv);
+  setup_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, sm.rw, sm.rs);
   __syncthreads();
 
   // K extent in bytes of the staged (MFMA) format; a multiple of 128
@@ -205,7 +218,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
   } else {
     const size_t rows = (size_t)p.max_blocks * BM;
-    xrs = tile_rsrc(p.h, (uint32_t)(rows * p.ld_h * (kQuantA ? 2 : esz)));
+    xrs = tile_rsrc(p.h, (uint32_t)(rows * h_row_bytes<FMT>(p)));
     if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
   }
   uint32_t xoff[CPT];
@@ -220,7 +233,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     } else if (STAGE == 1) {
       xoff[u] = (uint32_t)((size_t)tok * p.H * esz) + c * 16;
     } else {
-      xoff[u] = (uint32_t)(((size_t)b * BM + r) * p.ld_h * (kQuantA ? 2 : esz)) + c * 16 * XG;
+      xoff[u] = (uint32_t)(((size_t)b * BM + r) * h_row_bytes<FMT>(p)) + c * 16;
     }
   }
   uint32_t xsoff = kTileOutOfRange;  // the row's e8m0 scales (MX), for threads tid < BM
@@ -256,15 +269,13 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   // token-row register sets in flight: XD = 2 keeps the rows of K tiles
   // kt + 1 and kt + 2 loading while tile kt is multiplied
-  constexpr int XD = (kQuantA || (FMT == FMT_A8W8 && NB == 8)) ? 1 : 2;
-  uint4 xr[XD][CPT][XG];
+  constexpr int XD = (FMT == FMT_A8W8 && STAGE == 1 && NB == 8) ? 1 : 2;
+  uint4 xr[XD][CPT];
   uint32_t xsr[XD] = {};
   auto load_x = [&](int set, int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
-#pragma unroll
-      for (int h = 0; h < XG; ++h) xr[set][u][h] = tile_load16(xrs, xoff[u] + h * 16, (uint32_t)kt * 128 * XG);
+    for (int u = 0; u < CPT; ++u) xr[set][u] = tile_load16(xrs, xoff[u], (uint32_t)kt * 128);
     if constexpr (FMT == FMT_MX) {
       if (tid < BM) xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);
     }
@@ -273,21 +284,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int q = tid + kTileThreads * u;
-      uint4 v;
-      if constexpr (kQuantA) {
-        const float inv = sm.inv[(q / 128) * 16 + (q % 16)];
-        const uint32_t w[8] = {xr[set][u][0].x, xr[set][u][0].y, xr[set][u][0].z, xr[set][u][0].w,
-                               xr[set][u][1].x, xr[set][u][1].y, xr[set][u][1].z, xr[set][u][1].w};
-        uint32_t o[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          o[t] = pack4_e4m3(bf16_to_f32(w[2 * t] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t] >> 16) * inv,
-                            bf16_to_f32(w[2 * t + 1] & 0xFFFFu) * inv, bf16_to_f32(w[2 * t + 1] >> 16) * inv);
-        v = make_uint4(o[0], o[1], o[2], o[3]);
-      } else {
-        v = xr[set][u][0];
-      }
-      *reinterpret_cast<uint4*>(&sm.x[buf][q * 16]) = v;
+      *reinterpret_cast<uint4*>(&sm.x[buf][q * 16]) = xr[set][u];
     }
     if constexpr (FMT == FMT_MX) {
       if (tid < BM) sm.xsc[buf][tid] = xsr[set];
@@ -613,8 +610,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
 // Waves per SIMD the register allocation targets: two workgroups per CU keep
 // twice the loads in flight, where the operand registers allow it without
-// spilling (bf16; a8w8 except the 128-row stage 2, which also quantises h
-// while staging it; 32-row blocks).
+// spilling much (bf16; a8w8 except the 128-row stage 2; 32-row blocks).
 template <int FMT, int STAGE, int NB>
 constexpr int tile_waves_per_eu() {
   return (FMT == FMT_BF16 || (FMT == FMT_A8W8 && (STAGE == 1 || NB <= 4)) || NB <= 2) ? 2 : 1;
@@ -637,7 +633,8 @@ void gemm_tile_kernel(GemmParams p) {
   const int active = nblk * n_col;
   if ((int)blockIdx.x >= active) return;
   const int lt = (STAGE == 1) ? xcd_remap((int)blockIdx.x, active) : (int)blockIdx.x;
-  const int b = lt / n_col, nc = lt % n_col;
+  int b = lt / n_col, nc = lt % n_col;
+  if (STAGE == 1 && !p.dense && p.offsets) expert_major(p, BM, n_col, lt, b, nc);
   const int n0 = nc * WCOLS;
 
   const int e = p.dense ? -1 : p.block_expert[b];
@@ -689,7 +686,8 @@ void gemm_tile_accum_kernel(GemmParams p) {
       const int it = sm.item;
       __syncthreads();
       if (it >= items_q) break;
-      const int b = it / groups_q, j = it % groups_q;
+      int b = it / groups_q, j = it % groups_q;
+      if (p.offsets) expert_major(p, BM, groups_q, it, b, j);
       const int t = q + kNumXcd * (4 * j + wv);
       const bool wave_ok = t < n64;
       const ExpertView ev = resolve_expert<FMT, 2>(p, p.block_expert[b]);

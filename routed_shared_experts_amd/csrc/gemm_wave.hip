@@ -10,8 +10,8 @@
 // block's (at most 16) tokens the N dimension.  The K tile is the outer loop:
 // each 128-byte activation tile is read once and feeds all NCG x (gate, up)
 // weight tiles.  Weights are in the tiled layout, so the wave's 16 rows of one
-// K tile are two contiguous 1024-byte loads, which go from HBM straight into
-// MFMA operand registers, D K-tiles ahead; the activation rows come from L2
+// K tile are two contiguous 1024-byte non-temporal loads, which go from HBM
+// straight into MFMA operand registers, D K-tiles ahead; the activation rows come from L2
 // through a buffer descriptor (a padding row reads past the end of the
 // buffer, i.e. zeros, with no branch and no fetch).  There is no LDS and no
 // barrier: the many small independent workgroups hide each other's start-up
@@ -47,10 +47,8 @@ template <int FMT, int STAGE, int D>
 __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   constexpr int esz = FmtInfo<FMT>::esz;
   constexpr int BM = 16;
-  constexpr bool kQuantA = (STAGE == 2 && FMT == FMT_A8W8);
   constexpr int NW = (STAGE == 1) ? 2 : 1;    // weight rows per lane and group: gate + up, or W2
-  constexpr int NX = kQuantA ? 4 : 2;         // 16-byte activation loads per K tile
-  constexpr int NCG = (STAGE == 1) ? 2 : 4;   // 16-column groups per wave
+  constexpr int NCG = (STAGE == 1) ? 2 : 4;   // 16-column groups per wave (a multiple of 4 in stage 2)
   constexpr int CW = 16 * NCG;                // columns per wave
 
   const int lane = threadIdx.x;
@@ -111,8 +109,8 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
       const size_t off = tile_off(ev, rb, kt);
 #pragma unroll
       for (int m = 0; m < NW; ++m) {
-        wb[d][cgi][m][0] = ld16(wbase[m] + off);
-        wb[d][cgi][m][1] = ld16(wbase[m] + off + 1024);
+        wb[d][cgi][m][0] = ld16_stream(wbase[m] + off);
+        wb[d][cgi][m][1] = ld16_stream(wbase[m] + off + 1024);
         if constexpr (FMT == FMT_MX) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
         else wsc[d][cgi][m] = 127;
       }
@@ -157,6 +155,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   }
   // ---- activations: this lane's token row through a buffer descriptor ----
   const bool xok = tok_l >= 0;
+  const float wgt_pair = (STAGE == 2 && pair_l >= 0) ? p.pair_w[pair_l] : 0.f;  // ACCUMULATE weight
   __amdgpu_buffer_rsrc_t xr, xsr;
   uint32_t xoff, xsoff = 0;
   if constexpr (STAGE == 1) {
@@ -168,66 +167,35 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     }
   } else {
     const size_t rows = (size_t)p.max_blocks * BM;
-    xr = wv_rsrc(p.h, (uint32_t)(rows * p.ld_h * (kQuantA ? 2 : esz)));
-    xoff = xok ? (uint32_t)((size_t)slot_l * p.ld_h * (kQuantA ? 2 : esz)) + g * 16 * (kQuantA ? 2 : 1)
-               : kWvOutOfRange;
+    xr = wv_rsrc(p.h, (uint32_t)(rows * h_row_bytes<FMT>(p)));
+    xoff = xok ? (uint32_t)((size_t)slot_l * h_row_bytes<FMT>(p)) + g * 16 : kWvOutOfRange;
     if constexpr (FMT == FMT_MX) {
       xsr = wv_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
       xsoff = xok ? (uint32_t)(slot_l * (p.ld_h / 32)) + g : kWvOutOfRange;
     }
   }
-  float xinv = 0.f, rs = 1.0f;  // A8W8: stage-2 row quantisation (448 / amax) and row scale
+  float rs = 1.0f;  // A8W8: stage 1 the token's x scale, stage 2 the row scale amax / 448
   if constexpr (FMT == FMT_A8W8) {
     if (STAGE == 1) {
       rs = xok ? static_cast<const float*>(p.x_s)[tok_l] : 0.f;
     } else {
       const float amax = xok ? static_cast<const float*>(p.h_s)[slot_l] : 0.f;
-      if (amax > 0.f) {
-        xinv = __fdiv_rn(448.0f, amax);
-        rs = __fdiv_rn(amax, 448.0f);
-      }
+      if (amax > 0.f) rs = __fdiv_rn(amax, 448.0f);
     }
   }
 
-  uint4 xb[D][NX];
+  uint4 xb[D][2];
   int xsc[D];
   auto load_x = [&](int d, int kt) {
-    if constexpr (kQuantA) {  // bf16 h: 32 bytes per 16-element chunk
-      const uint32_t o = xoff + (uint32_t)kt * 256;
-      xb[d][0] = wv_load16(xr, o);
-      xb[d][1] = wv_load16(xr, o + 16);
-      xb[d][2] = wv_load16(xr, o + 128);
-      xb[d][3] = wv_load16(xr, o + 144);
-    } else {
-      const uint32_t o = xoff + (uint32_t)kt * 128;
-      xb[d][0] = wv_load16(xr, o);
-      xb[d][1] = wv_load16(xr, o + 64);
-    }
+    const uint32_t o = xoff + (uint32_t)kt * 128;
+    xb[d][0] = wv_load16(xr, o);
+    xb[d][1] = wv_load16(xr, o + 64);
     if constexpr (FMT == FMT_MX)
       xsc[d] = (int)__builtin_amdgcn_raw_buffer_load_b8(xsr, (int)(xsoff + (uint32_t)kt * 4), 0, 0);
     else
       xsc[d] = 127;
   };
-  auto act = [&](int d, uint4& x0, uint4& x1) {
-    if constexpr (kQuantA) {  // e4m3 with the row's 448 / amax on the fly
-      uint32_t o[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 lo = xb[d][2 * h], hi = xb[d][2 * h + 1];
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[4 * h + u] = pack4_e4m3(bf16_to_f32(w[2 * u] & 0xFFFFu) * xinv, bf16_to_f32(w[2 * u] >> 16) * xinv,
-                                    bf16_to_f32(w[2 * u + 1] & 0xFFFFu) * xinv,
-                                    bf16_to_f32(w[2 * u + 1] >> 16) * xinv);
-      }
-      x0 = make_uint4(o[0], o[1], o[2], o[3]);
-      x1 = make_uint4(o[4], o[5], o[6], o[7]);
-    } else {
-      x0 = xb[d][0];
-      x1 = xb[d][1];
-    }
-  };
+
   // lane results: rows 4g..4g+3 of each group (columns c0 + 16 cgi + 4g + j),
   // token l16
   const float sc = rs * ev.wscale;
@@ -249,13 +217,12 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   for (int kt0 = 0; kt0 < nk; kt0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      uint4 x0, x1;
-      act(d, x0, x1);
 #pragma unroll
       for (int cgi = 0; cgi < NCG; ++cgi)
 #pragma unroll
         for (int m = 0; m < NW; ++m)
-          mfma_tile<FMT>(acc[cgi][m], wb[d][cgi][m][0], wb[d][cgi][m][1], x0, x1, wsc[d][cgi][m], xsc[d]);
+          mfma_tile<FMT>(acc[cgi][m], wb[d][cgi][m][0], wb[d][cgi][m][1], xb[d][0], xb[d][1], wsc[d][cgi][m],
+                         xsc[d]);
       load(d, kt0 + d + D);
     }
   }
@@ -325,9 +292,9 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
       }
       return;
     }
-    // ACCUMULATE: this pair's 64 columns with device-coherent stores
+    // ACCUMULATE: this pair's CW columns with device-coherent stores
     if (pair_l >= 0) {
-      const float wgt = p.pair_w[pair_l];
+      const float wgt = wgt_pair;
       uint64_t* dst = reinterpret_cast<uint64_t*>(p.pair_out + (size_t)pair_l * p.H + c0 + 4 * g);
 #pragma unroll
       for (int cgi = 0; cgi < NCG; ++cgi)
@@ -338,18 +305,25 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
           __hip_atomic_store(dst + cgi * 8 + h, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // count the arrival once the stores are acknowledged (no agent-scope fence:
-    // on multi-XCD parts it would write back and invalidate the whole L2)
+    // count the arrivals (one per 64-column reduction tile) once the stores
+    // are acknowledged (no agent-scope fence: on multi-XCD parts it would
+    // write back and invalidate the whole L2)
     __builtin_amdgcn_s_waitcnt(0);
+    constexpr int NT = NCG / 4;
     const int n_tiles = p.H / 64;
-    const int tile = c0 / 64;
-    int done = 0;
-    if (g == 0 && pair_l >= 0) {
-      const int old = atomicAdd(p.counters + (size_t)tok_l * n_tiles + tile, 1);
-      done = (old == p.expected - 1);
+    const int t0 = c0 / 64;
+    int old[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      old[tt] = -1;
+      if (g == 0 && pair_l >= 0) old[tt] = atomicAdd(p.counters + (size_t)tok_l * n_tiles + t0 + tt, 1);
     }
-    done = __shfl(done, l16, kWave);  // broadcast to the token's 4 lanes
-    if (done) last_arrival_sum16(p, tok_l, c0 + 16 * g);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      // broadcast to the token's 4 lanes
+      const int done = __shfl(old[tt], l16, kWave) == p.expected - 1;
+      if (done) last_arrival_sum16(p, tok_l, 64 * (t0 + tt) + 16 * g);
+    }
   }
 }
 
@@ -372,6 +346,8 @@ static int wave_depth(const GemmParams& p, int stage, int fmt) {
   return (g % 2 == 0 && cap >= 2) ? 2 : 1;
 }
 
+// (64 columns per stage-2 wave measured best for decode batches: 32 or 128
+// columns per wave stream slower on MI355X)
 template <int FMT, int STAGE>
 static hipError_t launch_wv(const GemmParams& p, int depth, hipStream_t s) {
   constexpr int CW = (STAGE == 1) ? 32 : 64;

@@ -67,6 +67,7 @@ struct GemmParams {
   const int32_t* sorted;
   const int32_t* block_expert;
   const int32_t* num_blocks;
+  const int32_t* offsets;  // [E' + 1] padded row offsets of the experts (sort output), or NULL
   uint8_t* h;
   void* h_s;
   int ld_h;
