@@ -300,7 +300,10 @@ typedef struct {
   /* stage-1 output h, one row per sorted slot (dense: per token), row stride
    * ld_h = I (sorted) or I_s (dense): F32/BF16 values; MXFP8: codes + e8m0
    * h_scale [rows][ld_h/32]; A8W8: BF16 values + h_scale = fp32 row amax
-   * [rows] (must be zero before stage 1; stage 2 derives the row scale). */
+   * [rows] (must be zero before stage 1; stage 2 derives the row scale).
+   * A8W8 stage 2 first quantises every row of h in place (the e4m3 codes
+   * v * 448 / amax go to the first ld_h bytes of the row's 2*ld_h-byte
+   * storage), so h holds codes, not BF16 values, after moe_stage2_accum. */
   void* h;
   void* h_scale;
   /* stage 2 */
