@@ -77,8 +77,10 @@ __device__ __forceinline__ uint4 tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
 // the concurrent workgroups of an expert share each weight tile through L2
 // instead of streaming the expert's weights once per block.  In: the item
 // index `it` of block-major order; out: block b and column tile c.
+__device__ __forceinline__ int split_of(const GemmParams& p) { return p.bsplit > 1 ? p.bsplit : 1; }
+
 __device__ __forceinline__ void expert_major(const GemmParams& p, int BM, int n_per, int it, int& b, int& c) {
-  const int e = p.block_expert[it / n_per];
+  const int e = p.block_expert[it / n_per / split_of(p)];
   const int bs = p.offsets[e] / BM, nb = (p.offsets[e + 1] - p.offsets[e]) / BM;
   const int local = it - bs * n_per;
   c = local / nb;
@@ -660,7 +662,8 @@ void gemm_tile_accum_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n64 = p.H / 64;
-  const int nblk = *p.num_blocks;
+  const int nblk = *p.num_blocks * split_of(p);
+  const int P = p.T * p.k_total;
   int* q_next = p.counters + (size_t)p.T * n64;
   int* q_owner = q_next + kNumXcd;
   const int me = xcc_id();
@@ -690,7 +693,10 @@ void gemm_tile_accum_kernel(GemmParams p) {
       if (p.offsets) expert_major(p, BM, groups_q, it, b, j);
       const int t = q + kNumXcd * (4 * j + wv);
       const bool wave_ok = t < n64;
-      const ExpertView ev = resolve_expert<FMT, 2>(p, p.block_expert[b]);
+      // split blocks: a part holding only padding rows has nothing to do
+      // (padding sits at the end of an expert's rows)
+      if (split_of(p) > 1 && p.sorted[(size_t)b * BM] >= P) continue;
+      const ExpertView ev = resolve_expert<FMT, 2>(p, p.block_expert[b / split_of(p)]);
       tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok);
       __syncthreads();  // the next item rewrites the row tables
     }

@@ -68,6 +68,10 @@ struct GemmParams {
   const int32_t* block_expert;
   const int32_t* num_blocks;
   const int32_t* offsets;  // [E' + 1] padded row offsets of the experts (sort output), or NULL
+  // bsplit > 1: the launch runs each sorted block of block_m * bsplit rows as
+  // bsplit blocks of block_m rows (block_expert and num_blocks count the
+  // sorted blocks); 0 or 1: no split
+  int bsplit;
   uint8_t* h;
   void* h_s;
   int ld_h;
