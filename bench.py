@@ -83,7 +83,9 @@ def measured_traffic(workload):
 
 
 def algorithmic(cfg, ids, m_pseudo):
-    """Algorithmic FLOPs and bytes of the layer and of routed stage 1."""
+    """Algorithmic FLOPs and bytes of the layer, of stage 1 and of stage 2
+    (each stage: its weights once, its activation input once, its output once;
+    the shared expert's rows count in the stages when it runs as pseudo-experts)."""
     import workloads
     bw = workloads.bytes_per_weight(cfg.fmt)
     bx = {"f32": 4, "bf16": 2, "mxfp8": 2, "a8w8": 1}[cfg.fmt]
@@ -103,7 +105,11 @@ def algorithmic(cfg, ids, m_pseudo):
     s1_w = active * 2.0 * H * I * bw + (2.0 * H * Is * bw if (Is and m_pseudo) else 0.0)
     s1_bytes = s1_w + T * H * bx + (P + (T * m_pseudo if m_pseudo else 0)) * I * bh
     s1_flops = 4.0 * H * I * P + (4.0 * H * Is * T if m_pseudo else 0.0)
-    return flops, byt, s1_flops, s1_bytes, active
+    # stage 2: W2 once, h read once, out written once
+    s2_w = active * 1.0 * H * I * bw + (1.0 * H * Is * bw if (Is and m_pseudo) else 0.0)
+    s2_bytes = s2_w + (P + (T * m_pseudo if m_pseudo else 0)) * I * bh + T * H * bo
+    s2_flops = 2.0 * H * I * P + (2.0 * H * Is * T if m_pseudo else 0.0)
+    return flops, byt, (s1_flops, s1_bytes), (s2_flops, s2_bytes), active
 
 
 def cpu_baseline(cfg, inp, seconds):
@@ -216,7 +222,7 @@ def main():
                 renormalize=cfg.renormalize, routed_scaling_factor=cfg.routed_scaling_factor)
     torch.cuda.synchronize()
     m_pseudo = cfg.n_pseudo if best == "pseudo" else 0
-    flops, byt, s1_flops, s1_bytes, active = algorithmic(cfg, ids.cpu().numpy(), m_pseudo)
+    flops, byt, s1, s2, active = algorithmic(cfg, ids.cpu().numpy(), m_pseudo)
     rec = {
         "metric": METRIC,
         "value": cfg.T / (ms * 1e-3),
@@ -240,13 +246,25 @@ def main():
         "modes_ms": {k: v[0] / args.steps * 1e3 for k, v in results.items()},
     }
     if stage is not None:
-        s1_ms = stage["stage1"]
         rec["kernels_ms"] = stage
-        rec["roofline"] = {"kernel": "gemm stage 1 (routed gate/up + SiLU-mul)", "bound": "hbm",
-                           "achieved": s1_bytes / (s1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": s1_bytes / (s1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "traffic": measured_traffic(cfg.name) if best == "pseudo" else None,
-                           "bytes_per_launch": s1_bytes, "flops_per_launch": s1_flops,
+        # the dominant GEMM stage, against HBM or the MFMA peak of its dtype,
+        # whichever its arithmetic intensity makes the bound
+        st = "stage1" if stage["stage1"] >= stage["stage2"] else "stage2"
+        s_flops, s_bytes = s1 if st == "stage1" else s2
+        s_ms = stage[st]
+        peak_f = MFMA_PEAK_TFLOPS[cfg.fmt]
+        mfma_bound = s_flops / s_bytes > peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+        names = {"stage1": "gemm stage 1 (routed gate/up + SiLU-mul)",
+                 "stage2": "gemm stage 2 (down + weighted reduction onto the addend)"}
+        if mfma_bound:
+            ach, peak, unit = s_flops / (s_ms * 1e-3) / 1e12, peak_f, "TFLOP/s"
+        else:
+            ach, peak, unit = s_bytes / (s_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        rec["roofline"] = {"kernel": names[st], "bound": "mfma" if mfma_bound else "hbm",
+                           "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                           "traffic": (measured_traffic(cfg.name)
+                                       if (best == "pseudo" and st == "stage1" and not mfma_bound) else None),
+                           "bytes_per_launch": s_bytes, "flops_per_launch": s_flops,
                            "timed_steps": len(range(0, args.steps, TIMING_EVERY))}
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * 2**20) // 16 * 16

@@ -52,16 +52,23 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(SortParams p) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int nE = p.n_experts, BM = p.block_m;
   const int nchunk = (p.P + kChunk - 1) / kChunk;
-  // per expert: exclusive prefix over chunks (relative), total count
-  for (int e = tid; e < nE; e += kSortThreads) {
-    int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const size_t i = (size_t)c * nE + e;
-      const int v = p.chunk_base[i];
-      p.chunk_base[i] = run;
-      run += v;
+  // per-expert totals: every (chunk, expert) count once, all loads in flight
+  // together (coalesced over experts), summed with LDS atomics
+  for (int e = tid; e < nE; e += kSortThreads) s_count[e] = 0;
+  __syncthreads();
+  const int ncount = nchunk * nE;
+  for (int base = 0; base < ncount; base += 8 * kSortThreads) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kSortThreads + tid;
+      v[u] = i < ncount ? p.chunk_base[i] : 0;
     }
-    s_count[e] = run;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kSortThreads + tid;
+      if (i < ncount && v[u]) atomicAdd(&s_count[i % nE], v[u]);
+    }
   }
   __syncthreads();
   if (wv == 0) {
@@ -87,7 +94,19 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(SortParams p) {
   for (int e = tid; e < nE; e += kSortThreads) {
     p.counts[e] = s_count[e];
     p.offsets[e] = s_off[e];
-    for (int c = 0; c < nchunk; ++c) p.chunk_base[(size_t)c * nE + e] += s_off[e];
+    // chunk bases: the expert's offset plus the exclusive prefix of its counts
+    // over the chunks, 16 chunks' loads in flight at a time
+    int run = s_off[e];
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < nchunk ? p.chunk_base[(size_t)(c0 + u) * nE + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (c0 + u < nchunk) p.chunk_base[(size_t)(c0 + u) * nE + e] = run;
+        run += v[u];
+      }
+    }
     for (int i = s_off[e] + s_count[e]; i < s_off[e + 1]; ++i) p.sorted[i] = p.P;
   }
   if (tid == 0) {

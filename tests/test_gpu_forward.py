@@ -52,6 +52,21 @@ def test_block_m_variants(gpu, block_m):
     assert_close(cfg, out, inp)
 
 
+@pytest.mark.parametrize("T", [64, 65])
+@pytest.mark.parametrize("mode", ["pseudo", "aux"])
+def test_decode_blocks_with_many_tokens_per_expert(gpu, T, mode):
+    """16-row blocks at T <= 64 find their pairs by scanning the routing ids
+    (block = sub-block * E' + expert, no sort launch); heavily skewed routing
+    gives an expert nearly every token, i.e. several sub-blocks, and so do the
+    two pseudo chunks.  T = 65 takes the sorted path with the same blocks."""
+    cfg = LC(f"skew{T}", T=T, H=256, E=8, I=128, I_s=256, topk=2, fmt="bf16", logits="zipf", zipf_s=2.0)
+    inp = inputs(cfg, gpu)
+    ids = workloads.to_host(inp)["logits"].argmax(axis=1)
+    assert np.bincount(ids, minlength=cfg.E).max() > 32  # the top expert spans three or more sub-blocks
+    out, _ = run_forward(cfg, inp, mode, block_m=16)
+    assert_close(cfg, out, inp)
+
+
 @pytest.mark.parametrize("mode", ["pseudo", "aux"])
 def test_tiny_f32_workload(gpu, mode):
     cfg = workloads.CONFIGS["tiny_f32"]
