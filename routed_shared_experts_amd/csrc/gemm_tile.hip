@@ -271,7 +271,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   // token-row register sets in flight: XD = 2 keeps the rows of K tiles
   // kt + 1 and kt + 2 loading while tile kt is multiplied
-  constexpr int XD = (FMT == FMT_A8W8 && STAGE == 1 && NB == 8) ? 1 : 2;
+  constexpr int XD = ((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) ? 1 : 2;
   uint4 xr[XD][CPT];
   uint32_t xsr[XD] = {};
   auto load_x = [&](int set, int kt) {
@@ -314,7 +314,36 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // issuing loads (measured: a8w8 stage 1 -5 %, bf16 and MX unchanged).
   auto compute = [&](int buf, const uint4 (&w)[4][2], const int (&sc)[4]) {
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (k32) {
+    if constexpr (k32 && STAGE == 1) {
+      // four K steps of 16; the token fragments of step st + 1 are read
+      // while step st multiplies (LDS latency behind eight MFMAs); the
+      // scheduling groups pin that order (the default schedule reads each
+      // fragment just before its two MFMAs and exposes the LDS latency)
+      __builtin_amdgcn_sched_barrier(0);
+      uint4 bf[2][NN];
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn)
+        bf[0][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st < 3) {
+#pragma unroll
+          for (int nn = 0; nn < NN; ++nn)
+            bf[(st + 1) & 1][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32 + 512 * (st + 1)]);
+          __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
+        }
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+            acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf[st & 1][nn]),
+                acc32[mm][nn], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NN, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (k32) {
       // four K steps of 16; consecutive MFMAs update different accumulators
 #pragma unroll
       for (int st = 0; st < 4; ++st)
