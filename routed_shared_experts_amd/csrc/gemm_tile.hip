@@ -16,10 +16,14 @@
 // loads a 16-row fragment of a K tile as two contiguous 1 KiB reads straight
 // into MFMA operand registers: weights never pass through LDS, and no two
 // waves load the same weight bytes.  The gathered token rows are shared by the
-// four waves, so they are staged through LDS, double buffered, in the same
-// operand order (each 16-row x 128-byte fragment is 2 KiB, lane-contiguous),
-// which makes both the LDS writes and the ds_read_b128 fragment reads free of
-// bank conflicts without a swizzle.
+// four waves, so they are staged through LDS, double buffered.  Each lane
+// loads one 16-byte chunk and eight consecutive lanes one row's whole
+// 128-byte K tile (a wave touches eight full cache lines; reading 64 bytes
+// of sixteen rows instead costs measurably more L1/L2 traffic).  In LDS a
+// 16-row x 128-byte fragment is 2 KiB in operand order (chunk c of row r at
+// (c / 4) * 1024 + (c % 4) * 256 + 16 * slot) with the row slot XOR-swizzled,
+// slot = r ^ c ^ 8 (r & 1), so that the row-wise writes and the
+// operand-order ds_read_b128 fragment reads are both free of bank conflicts.
 //
 // Workgroup = 4 waves x 64 weight rows: in stage 1 a wave owns 32 h columns
 // (32 gate rows + the matching 32 up rows, so SiLU-mul happens in registers),
@@ -89,7 +93,7 @@ __device__ __forceinline__ void expert_major(const GemmParams& p, int BM, int n_
 
 template <int BM>
 struct TileSmem {
-  uint8_t x[2][BM * 128];  // staged token rows, operand order
+  uint8_t x[2][BM * 128];  // staged token rows, swizzled operand order
   uint32_t xsc[2][BM];     // MX: the rows' e8m0 scales of the staged K tile
   int tok[BM];
   int pair[BM];
@@ -97,6 +101,14 @@ struct TileSmem {
   float rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
   int item;       // persistent stage 2: the claimed work item / queue
 };
+
+// LDS offset of 16-byte chunk c (0..7) of row r (0..15) in a staged 16-row
+// fragment: operand order, row slot XOR-swizzled.  For a fixed row the eight
+// chunks land in eight different 16-byte bank groups (and rows r, r + 1 in
+// the other eight), and for a fixed chunk the sixteen rows in sixteen.
+__device__ __forceinline__ int lds_chunk_off(int r, int c) {
+  return (c / 4) * 1024 + (c % 4) * 256 + ((r ^ c ^ ((r & 1) << 3)) & 15) * 16;
+}
 
 // Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
 // k_total pair rows in slot order, one rounding.  Same arithmetic as
@@ -212,8 +224,8 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   const uint32_t kfrag32 = (uint32_t)(((lane / 32) * 16 + l16) * 16);
   const uint32_t wlane = k32 ? (uint32_t)(((lane % 32) / 16) * ev.nkt * 2048) + kfrag32 : (uint32_t)lane * 16;
 
-  // ---- staged token rows: chunk q = tid + 256 u is (row block q/128, half,
-  // lane group, row) in operand order; padding rows read past the buffer ----
+  // ---- staged token rows: chunk q = tid + 256 u is chunk q % 8 of row q / 8;
+  // padding rows read past the buffer ----
   __amdgpu_buffer_rsrc_t xrs, xsrs;
   if (STAGE == 1) {
     xrs = tile_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * esz));
@@ -223,12 +235,15 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     xrs = tile_rsrc(p.h, (uint32_t)(rows * h_row_bytes<FMT>(p)));
     if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
   }
+  // LDS offset of chunk u: row tid / 8 + 32 u sits two 16-row fragments
+  // (4 KiB) further on per u, with the same swizzle
+  const uint32_t soff = (uint32_t)(lds_chunk_off((tid / 8) % 16, tid % 8) + (tid / 128) * 2048);
   uint32_t xoff[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int q = tid + kTileThreads * u;
-    const int r = (q / 128) * 16 + (q % 16);
-    const int c = ((q / 64) % 2) * 4 + (q / 16) % 4;  // 16-byte chunk of the 128-byte K tile
+    const int r = q / 8;
+    const int c = q % 8;  // 16-byte chunk of the 128-byte K tile
     const int tok = sm.tok[r];
     if (tok < 0) {
       xoff[u] = kTileOutOfRange;
@@ -285,8 +300,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   auto store_x = [&](int buf, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int q = tid + kTileThreads * u;
-      *reinterpret_cast<uint4*>(&sm.x[buf][q * 16]) = xr[set][u];
+      *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
     }
     if constexpr (FMT == FMT_MX) {
       if (tid < BM) sm.xsc[buf][tid] = xsr[set];
@@ -306,8 +320,13 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc32[mm][nn][v] = 0.f;
-  // k32 token fragment of lane l: row block (l % 32) / 16 of a 32-row group
-  const uint32_t xfrag32 = (uint32_t)(((lane % 32) / 16) * 2048) + kfrag32;
+  // k32 token fragment of lane l at K step st: row l % 16 of row block
+  // (l % 32) / 16 of a 32-row group, chunk 2 st + l / 32; the swizzle of step
+  // st is that of step 0 with slot bits 1-2 flipped (XOR 32 st on the offset)
+  const uint32_t xfrag32 = (uint32_t)(((lane % 32) / 16) * 2048 + lds_chunk_off(l16, lane / 32));
+  auto xf32 = [&](int st) { return (xfrag32 ^ (uint32_t)(32 * st)) + (uint32_t)(512 * st); };
+  // 16x16 operands: lane (g, r) takes chunks g and 4 + g of row r
+  const uint32_t xo0 = (uint32_t)lds_chunk_off(l16, g), xo1 = (uint32_t)lds_chunk_off(l16, 4 + g);
 
   // The multiply of a K tile runs at raised wave priority, so a wave with its
   // operands ready keeps the matrix core busy ahead of the SIMD's other wave
@@ -323,14 +342,14 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       uint4 bf[2][NN];
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn)
-        bf[0][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32]);
+        bf[0][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(0)]);
       __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         if (st < 3) {
 #pragma unroll
           for (int nn = 0; nn < NN; ++nn)
-            bf[(st + 1) & 1][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32 + 512 * (st + 1)]);
+            bf[(st + 1) & 1][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st + 1)]);
           __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
         }
 #pragma unroll
@@ -349,32 +368,18 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
-          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xfrag32 + 512 * st]);
+          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st)]);
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm)
             acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf), acc32[mm][nn],
                 0, 0, 0);
         }
-    } else if constexpr (FMT == FMT_BF16) {
-      // two K=32 halves; the half is the outer loop so that consecutive MFMAs
-      // update different accumulators
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + h * 1024 + lane * 16]);
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[mb][h]),
-                                                                  __builtin_bit_cast(bf16x8, bf), acc[mb][nb], 0, 0, 0);
-        }
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const uint8_t* frag = &sm.x[buf][nb * 2048 + lane * 16];
-        const uint4 b0 = *reinterpret_cast<const uint4*>(frag);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(frag + 1024);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo0]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo1]);
         const int sb = (FMT == FMT_MX) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) mfma_tile<FMT>(acc[mb][nb], w[mb][0], w[mb][1], b0, b1, sc[mb], sb);
