@@ -181,7 +181,11 @@ size_t moe_workspace_bytes(const moe_forward_args* a);
  *   PSEUDO/NONE: prologue (route + gate dot + MX quant of x) -> sort (also
  *                clears the arrival counters) -> stage 1 -> stage 2 (per-pair
  *                rows; the last arrival per (token, column tile) sums them in
- *                slot order and rounds once into out).
+ *                slot order and rounds once into out).  At T <= 64 with
+ *                16-row blocks there is no sort launch (each block finds its
+ *                pairs itself), and with softmax scores over E <= 64 experts
+ *                (E a multiple of 4, no groups, bf16/fp32) the routing runs
+ *                inside the stage-1 launch: stage 1 -> stage 2.
  *   AUX:         main runs the prologue and records ev_fork; aux waits on it
  *                and runs dense shared stage 1 and shared stage 2 (STORE of
  *                gamma*S(x) into the addend buffer), then records ev_ready.

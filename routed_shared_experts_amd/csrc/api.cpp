@@ -585,7 +585,14 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
     rp.zero_ptr = sp.zero_ptr;
     rp.zero_vec = sp.zero_vec;
   }
-  HIP_TRY(launch_route(rp, main_s));
+  // Self-sorted stage 1 with softmax scores over at most 64 experts (no
+  // groups) and nothing else in the prologue that stage 1 reads (no MX
+  // quantisation of x, no a8w8 row maxima to clear) runs the routing inside
+  // its own launch; the aux stream needs gamma before stage 1, so not with it.
+  const bool fuse_route = pl.self_sort && !aux && a->score == MOE_SCORE_SOFTMAX && a->n_group <= 1 &&
+                          (fmt == FMT_BF16 || fmt == FMT_F32) && a->E <= 64 && a->E % 4 == 0 &&
+                          aligned16(a->logits);
+  if (!fuse_route) HIP_TRY(launch_route(rp, main_s));
   if (tev) HIP_TRY(hipEventRecord(tev[1], main_s));
 
   GemmParams g{};
@@ -638,6 +645,8 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.block_m = pl.block_m;
   g.max_blocks = pl.self_sort ? pl.ss_blocks : pl.max_blocks;
   g.self_sort = pl.self_sort;
+  g.route_fused = fuse_route;
+  if (fuse_route) g.route = rp;
   g.ids = ids;
   g.sorted = sorted;
   g.block_expert = bexp;

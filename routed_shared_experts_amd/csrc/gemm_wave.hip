@@ -26,6 +26,7 @@
 // each 128-byte K tile (the gfx950 16x16x128 f8f6f4 operand order); MX scales
 // come from lane r + 16b for K block b.
 #include "gemm_common.hpp"
+#include "prologue.hpp"
 
 namespace moe {
 
@@ -43,6 +44,38 @@ __device__ __forceinline__ uint4 wv_load16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// Whether expert e < E <= 64 (E a multiple of 4) is among token t's top-k
+// under the routing's own rule (route_token with softmax scores and no
+// groups): fewer than topk experts have a larger selection key (logit bits,
+// then the lower index).
+__device__ __forceinline__ bool expert_selected(const RouteParams& r, int t, int e) {
+  const float* lr = r.logits + (size_t)t * r.E;
+  const uint64_t ke = ((uint64_t)float_key(lr[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  int above = 0;
+#pragma unroll 4
+  for (int f = 0; f < r.E; f += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(lr + f);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      above += (((uint64_t)float_key(vv[q]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(f + q))) > ke;
+  }
+  return above < r.topk;
+}
+
+// The routing workgroups of a fused stage-1 launch (E <= 64): workgroup
+// w < T routes token w (ids, weights, gamma), the rest clear the stage-2
+// counters.
+__device__ __forceinline__ void fused_route_wave(const GemmParams& p, int first, int lane) {
+  __shared__ float sel[kWave], val[kWave];
+  const int w = (int)blockIdx.x - first;
+  if (w >= p.route.T) {
+    clear_region(p.route.zero_ptr, p.route.zero_vec, first + p.route.T);
+    return;
+  }
+  route_token<1>(p.route, w, lane, sel, val);
+}
+
 template <int FMT, int STAGE, int D>
 __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   constexpr int esz = FmtInfo<FMT>::esz;
@@ -55,6 +88,10 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   const int g = lane / 16, l16 = lane % 16;
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const int ncw = width_max / CW;
+  if (STAGE == 1 && p.route_fused && (int)blockIdx.x >= p.max_blocks * ncw) {
+    fused_route_wave(p, p.max_blocks * ncw, lane);
+    return;
+  }
   const int b = blockIdx.x / ncw, c0 = (blockIdx.x % ncw) * CW;
 
   // block expert and this lane's token (sorted blocks: fetched together)
@@ -130,7 +167,17 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     __shared__ int s_pair[BM];
     const int P = p.T * p.k_total;
     int cum = 0;
-    for (int base = 0; base < P; base += 4 * kWave) {
+    if (STAGE == 1 && p.route_fused) {
+      // lane t: token t (T <= 64) selects expert e; pseudo experts take every
+      // token.  Ranks in token order are ranks in pair order; stage 1 needs
+      // only the token of a row (pair index with slot 0).
+      const bool hit = lane < p.T && (e >= p.E || expert_selected(p.route, lane, e));
+      const uint64_t m = __ballot(hit);
+      const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) - BM * sb;
+      if (hit && r >= 0 && r < BM) s_pair[r] = lane * p.k_total;
+      cum = (int)__popcll(m);
+    }
+    for (int base = 0; base < P && !(STAGE == 1 && p.route_fused); base += 4 * kWave) {
       int idv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -352,7 +399,8 @@ template <int FMT, int STAGE>
 static hipError_t launch_wv(const GemmParams& p, int depth, hipStream_t s) {
   constexpr int CW = (STAGE == 1) ? 32 : 64;
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
-  const dim3 grid((unsigned)(p.max_blocks * (width_max / CW)));
+  const long long route_wgs = (STAGE == 1 && p.route_fused) ? p.route.T + clear_blocks(p.route.zero_vec, 64) : 0;
+  const dim3 grid((unsigned)(p.max_blocks * (width_max / CW) + route_wgs));
   if (depth >= 2)
     hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 2>), grid, dim3(64), 0, s, p);
   else

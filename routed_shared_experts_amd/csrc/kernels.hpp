@@ -84,6 +84,14 @@ struct GemmParams {
   int mode;  // 0 store, 1 accumulate
   int32_t* counters;
   int expected;
+  // route_fused (self_sort stage 1, softmax scores without groups): the
+  // routing runs inside the stage-1 launch.  Each GEMM wave finds its
+  // expert's tokens from the router logits with the selection rule of the
+  // routing itself, and route.T workgroups after the GEMM grid route the
+  // tokens (ids, weights and gamma for stage 2), the ones after those clear
+  // route.zero_ptr
+  int route_fused;
+  RouteParams route;
 };
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
