@@ -94,7 +94,7 @@ __device__ __forceinline__ void expert_major(const GemmParams& p, int BM, int n_
 template <int BM>
 struct TileSmem {
   uint8_t x[2][BM * 128];  // staged token rows, swizzled operand order
-  uint32_t xsc[2][BM];     // MX: the rows' e8m0 scales of the staged K tile
+  uint32_t xsc[2][BM + 1];  // MX: the rows' e8m0 scales of the staged K tile, + a spare slot
   int tok[BM];
   int pair[BM];
   float rw[BM];   // stage 2: pair weight / gate
@@ -294,7 +294,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
     for (int u = 0; u < CPT; ++u) xr[set][u] = tile_load16(xrs, xoff[u], (uint32_t)kt * 128);
     if constexpr (FMT == FMT_MX) {
-      if (tid < BM) xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);
+      xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);  // tid >= BM: reads 0
     }
   };
   auto store_x = [&](int buf, int set) {
@@ -303,7 +303,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
     }
     if constexpr (FMT == FMT_MX) {
-      if (tid < BM) sm.xsc[buf][tid] = xsr[set];
+      sm.xsc[buf][tid < BM ? tid : BM] = xsr[set];  // no branch: the other threads write the spare slot
     }
   };
 
@@ -651,10 +651,10 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
 // Waves per SIMD the register allocation targets: two workgroups per CU keep
 // twice the loads in flight, where the operand registers allow it without
-// spilling much (bf16; a8w8 except the 128-row stage 2; 32-row blocks).
+// spilling much (bf16; 32- and 64-row blocks; 128-row a8w8 stage 1).
 template <int FMT, int STAGE, int NB>
 constexpr int tile_waves_per_eu() {
-  return (FMT == FMT_BF16 || (FMT == FMT_A8W8 && (STAGE == 1 || NB <= 4)) || NB <= 2) ? 2 : 1;
+  return (FMT == FMT_BF16 || NB <= 4 || (FMT == FMT_A8W8 && STAGE == 1)) ? 2 : 1;
 }
 
 // Stage 1 (and the dense STORE stage 2): one workgroup per (block, column
