@@ -67,14 +67,15 @@ def test_decode_blocks_with_many_tokens_per_expert(gpu, T, mode):
     assert_close(cfg, out, inp)
 
 
-@pytest.mark.parametrize("E", [64, 6])
+@pytest.mark.parametrize("E", [64, 6, 96])
 @pytest.mark.parametrize("T", [32, 64])
 def test_decode_routing_inside_stage1_with_tied_logits(gpu, T, E):
     """At decode sizes (16-row self-sorted blocks, softmax, E <= 64 and a
     multiple of 4, pseudo mode) the stage-1 launch routes the tokens itself and
     each GEMM wave selects its expert's tokens with the routing's rule; logits
-    in {-1, 0, 1} make most selections ties (lower index first).  E = 6 and
-    the aux mode take the separate routing launch; all must match the oracle."""
+    in {-1, 0, 1} make most selections ties (lower index first).  E = 6, E = 96
+    and the aux mode take the separate routing launch; all must match the
+    oracle."""
     cfg = LC(f"ties{T}_{E}", T=T, H=256, E=E, I=128, I_s=128, topk=min(8, E), fmt="bf16", logits="iid")
     inp = dict(inputs(cfg, gpu))
     rng = np.random.default_rng(T * 100 + E)
