@@ -133,7 +133,7 @@ typedef struct {
 
 /* Everything one layer forward needs. */
 typedef struct {
-  int32_t T, H, E, I, I_s, topk; /* I_s = 0: no shared expert */
+  int32_t T, H, E, I, I_s, topk; /* I_s = 0: no shared expert; T = 0: empty batch (a no-op) */
   /* routing */
   int32_t score;            /* moe_score */
   int32_t n_group;          /* 1 = no groups; E % n_group == 0 */
@@ -196,7 +196,8 @@ size_t moe_workspace_bytes(const moe_forward_args* a);
  * aligned; its contents on entry are irrelevant.  main/aux: distinct streams
  * in AUX mode (aux ignored otherwise).  ev_fork/ev_ready: caller-created
  * events (ignored unless AUX).  The workspace and the events must not be used
- * by an overlapping call. */
+ * by an overlapping call.  T = 0 returns MOE_OK after validation and touches
+ * nothing (workspace, streams and events may be NULL). */
 moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_bytes,
                        hipStream_t main, hipStream_t aux, hipEvent_t ev_fork,
                        hipEvent_t ev_ready);

@@ -84,7 +84,9 @@ struct Plan {
 
 moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (!a) return MOE_ERR_INVALID_ARG;
-  if (a->T <= 0 || a->H <= 0 || a->E <= 0 || a->I <= 0 || a->I_s < 0 || a->topk <= 0)
+  // T = 0 is an empty batch: valid, and then logits, x, out and the row
+  // scales may be NULL
+  if (a->T < 0 || a->H <= 0 || a->E <= 0 || a->I <= 0 || a->I_s < 0 || a->topk <= 0)
     return MOE_ERR_INVALID_ARG;
   if (a->E > 512 || a->topk > a->E) return MOE_ERR_INVALID_ARG;
   if (a->H % 16 || a->I % 16 || a->I_s % 16) return MOE_ERR_INVALID_ARG;
@@ -94,7 +96,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (a->group_score_topk != 1 && a->group_score_topk != 2) return MOE_ERR_INVALID_ARG;
   if (a->n_group > 1 && a->group_score_topk == 2 && a->E / a->n_group < 2) return MOE_ERR_INVALID_ARG;
   if ((long long)a->topk > (long long)a->topk_group * (a->E / a->n_group)) return MOE_ERR_INVALID_ARG;
-  if (!a->logits || !a->x || !a->out) return MOE_ERR_INVALID_ARG;
+  if (a->T > 0 && (!a->logits || !a->x || !a->out)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a->logits) || !aligned16(a->x) || !aligned16(a->out)) return MOE_ERR_INVALID_ARG;
   if (a->bias && ((uintptr_t)a->bias & 3u)) return MOE_ERR_INVALID_ARG;
   if (a->bias && a->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
@@ -111,7 +113,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if ((fmt == FMT_BF16 || fmt == FMT_MX) && a->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (fmt == FMT_A8W8) {
     if (a->x_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-    if (!a->x_row_scale || ((uintptr_t)a->x_row_scale & 3u)) return MOE_ERR_INVALID_ARG;
+    if ((a->T > 0 && !a->x_row_scale) || ((uintptr_t)a->x_row_scale & 3u)) return MOE_ERR_INVALID_ARG;
   }
   if (fmt == FMT_F32 && a->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   const int kt = ktile_elems(fmt);
@@ -516,6 +518,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   int fmt = -1;
   moe_status st = validate_impl(a, &fmt);
   if (st != MOE_OK) return st;
+  if (a->T == 0) return MOE_OK;  // empty batch: nothing to launch, workspace and streams untouched
   const Plan pl = make_plan(a, fmt);
   if (!workspace || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
   if (workspace_bytes < pl.off_end) return MOE_ERR_WORKSPACE;

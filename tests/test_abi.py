@@ -149,6 +149,21 @@ def test_validate_rejections():
     assert m.moe_validate(a) == m.MOE_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "a8w8_large"])
+def test_empty_batch_is_a_valid_no_op(name):
+    """T = 0: valid with NULL logits / x / out / row scales, a positive
+    workspace size, and moe_forward returns MOE_OK without a HIP call (no
+    workspace, streams or events needed) -- so it runs without a GPU."""
+    c = workloads.CONFIGS[name]
+    for mode in ("pseudo", "aux"):
+        a = _args(c, mode, T=0, logits=None, x=None, out=None, x_row_scale=None)
+        assert m.moe_validate(a) == m.MOE_OK
+        assert m.moe_workspace_bytes(a) > 0
+        assert m.lib().moe_forward(ctypes.byref(a), None, 0, None, None, None, None) == m.MOE_OK
+    assert m.moe_validate(_args(c, T=-1)) == m.MOE_ERR_INVALID_ARG
+    assert m.moe_validate(_args(c, x=None)) == m.MOE_ERR_INVALID_ARG  # T > 0 needs its inputs
+
+
 def test_forward_rejects_without_launching():
     """Invalid requests and a too-small workspace return before any HIP call,
     so they work on a machine without a GPU."""

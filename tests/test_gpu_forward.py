@@ -138,6 +138,19 @@ def test_a8w8_large_workload_sampled(gpu, mode):
     print(f"a8w8_large/{mode}: max|err|/rms={rel:.3e} floor={floor:.3e}")
 
 
+@pytest.mark.parametrize("mode", ["pseudo", "aux"])
+def test_empty_batch(gpu, mode):
+    """T = 0 through the binding: the forward succeeds, launches nothing and
+    leaves the stream usable."""
+    cfg = SMALL["small_bf16"]
+    inp = inputs(cfg, gpu)
+    empty = dict(inp, x=inp["x"][:0], logits=inp["logits"][:0])
+    out, _ = run_forward(cfg.replace(T=0), empty, mode)
+    assert tuple(out.shape) == (0, cfg.H)
+    out2, _ = run_forward(cfg, inp, mode)  # a full call right after
+    assert_close(cfg, out2, inp)
+
+
 def test_single_token_and_single_expert(gpu):
     cfg = LC("t1", T=1, H=128, E=1, I=64, I_s=64, topk=1, fmt="bf16", logits="iid")
     inp = inputs(cfg, gpu)
