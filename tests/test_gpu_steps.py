@@ -110,6 +110,24 @@ def test_route_grouped_with_ties_and_k_equals_e(gpu):
     assert np.array_equal(ids, rid) and np.abs(w - rw).max() <= 1e-6
 
 
+@pytest.mark.parametrize("E", [320, 512])
+def test_route_at_the_expert_and_slot_limits(gpu, E):
+    """E up to 512 routed experts (eight per lane) and k + pseudo slots up to
+    64, plain and grouped, against the oracle bit-exact."""
+    rng = np.random.default_rng(E)
+    lg = rng.normal(0, 1, (97, E)).astype(np.float32)
+    lg[::7] = np.round(lg[::7])  # some tie-heavy rows
+    lg_t = torch.from_numpy(lg).to(gpu)
+    ids, w = _route_gpu(lg_t, 48, n_pseudo=16, gamma=torch.full((97,), 0.25, device=gpu))
+    rid, rw = oracle.route(lg, topk=48)
+    assert np.array_equal(ids[:, :48], rid) and np.abs(w[:, :48] - rw).max() <= 1e-6
+    assert np.array_equal(ids[:, 48:], np.tile(np.arange(E, E + 16), (97, 1)))
+    bias = (rng.integers(-2, 3, E) * 0.0625).astype(np.float32)
+    ids, w = _route_gpu(lg_t, 8, score="sigmoid", bias=torch.from_numpy(bias).to(gpu), n_group=32, topk_group=4)
+    rid, rw = oracle.route(lg, topk=8, score="sigmoid", bias=bias, n_group=32, topk_group=4)
+    assert np.array_equal(ids, rid) and np.abs(w - rw).max() <= 1e-6
+
+
 def _sort_gpu(ids_np, n_experts, block_m, dev, zero=None, scratch=True):
     m = _m()
     T, k = ids_np.shape
