@@ -151,6 +151,16 @@ def test_empty_batch(gpu, mode):
     assert_close(cfg, out2, inp)
 
 
+@pytest.mark.parametrize("mode", ["pseudo", "aux"])
+def test_512_experts(gpu, mode):
+    """The largest expert count (eight logits per routing lane, 513-514
+    sort buckets with the pseudo chunks), most experts with one or two pairs."""
+    cfg = LC("e512", T=300, H=128, E=512, I=64, I_s=128, topk=8, fmt="bf16", logits="iid")
+    inp = inputs(cfg, gpu)
+    out, _ = run_forward(cfg, inp, mode)
+    assert_close(cfg, out, inp)
+
+
 def test_single_token_and_single_expert(gpu):
     cfg = LC("t1", T=1, H=128, E=1, I=64, I_s=64, topk=1, fmt="bf16", logits="iid")
     inp = inputs(cfg, gpu)
