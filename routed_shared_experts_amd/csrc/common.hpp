@@ -97,14 +97,6 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
 
 // ---- wave64 reductions through DPP (no LDS round trips) ----------------------
 // row_shr:1,2,4,8 leave each row's total in its lane 15; row_bcast:15 and
@@ -154,10 +146,6 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   f = f + 0.0f;
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_float(uint32_t k) {
-  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(u);
 }
 
 }  // namespace moe

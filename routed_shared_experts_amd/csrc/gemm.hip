@@ -9,13 +9,13 @@
 // the stage-2 input format (bf16, MX-32 e4m3, or bf16 plus a per-row amax
 // from which stage 2 derives the per-row e4m3 scale).
 //
-// Stage 2: o = h . W2[e]^T, times the scales; the epilogue adds pair_w * o
-// into the fp32 accumulator, which already holds the shared-expert addend
-// when the shared expert ran on the aux stream (vLLM PR 65207, commit 2: the
-// shared output is accumulated in the stage-2 epilogue instead of by a
-// separate add), and the last of the expected contributions to a
-// (token, column tile) rounds the fp32 sum once into the output.  In STORE
-// mode (dense shared expert) it writes gamma_t * o into the accumulator.
+// Stage 2: o = h . W2[e]^T, times the scales; the epilogue stores pair_w * o
+// as the pair's fp32 row, and the last of the expected contributions to a
+// (token, column tile) sums the addend (the shared expert's output when it ran
+// on the aux stream) and the token's pair rows in slot order and rounds the
+// fp32 sum once into the output (vLLM PR 65207, commit 2: the shared output is
+// accumulated in the stage-2 epilogue instead of by a separate add).  In
+// STORE mode (dense shared expert) it writes gamma_t * o into the addend.
 //
 // Tiles: 256 threads = 4 waves; BM sorted rows x BN output columns; the K tile
 // is 128 bytes of the operand format (32 fp32, 64 bf16 or 128 fp8 elements).
