@@ -316,8 +316,9 @@ typedef struct {
   const float* gamma;  /* dense: [T] gate values or NULL (= 1) */
   float* acc;          /* STORE: [T][H] fp32 destination of gamma_t * S(x_t);
                           ACCUMULATE: [T][H] fp32 addend, or NULL for none */
-  float* pair_out;     /* ACCUMULATE: [T*k_total][H] fp32, row t*k_total+j holds
-                          pair_w[t][j] * E_{e_tj}(x_t) (contents on entry irrelevant) */
+  float* pair_out;     /* ACCUMULATE: scratch of T*k_total*H*4 bytes for the
+                          per-pair rows pair_w[t][j] * E_{e_tj}(x_t), pair
+                          t*k_total+j (contents on entry and exit unspecified) */
   void* out;           /* [T][H] in out_dtype, written by the last arrival */
   int32_t out_dtype;
   int32_t mode;        /* STORE (dense only) or ACCUMULATE (sorted only) */
@@ -343,11 +344,14 @@ moe_status moe_stage1(const moe_stage_args* a, hipStream_t stream);
 
 /* Stage 2 with the shared-expert addend accumulated in its epilogue (vLLM PR
  * 65207, "Purpose", commit 2): o = h . W2[e]^T in fp32 times the scales.
- * ACCUMULATE stores pair_w * o as the pair's row of pair_out; the last of the
+ * ACCUMULATE stores pair_w * o as the pair's row in pair_out; the last of the
  * k_total contributions to a (token, 64-column tile) computes
- * addend + sum_j pair_out[t*k_total + j] in fp32, j in slot order, and rounds
- * it once into out (deterministic: the result does not depend on the order in
- * which workgroups finish).  STORE writes gamma_t * o into acc (the addend of
+ * addend + sum_j row[t*k_total + j] in fp32, j in slot order, and rounds it
+ * once into out (deterministic: the result does not depend on the order in
+ * which workgroups finish).  The one-wave kernels (16-row blocks) keep the
+ * rows in fp32; the 32-128-row kernels store each (pair, 64-column tile) as
+ * 16-bit codes with one power-of-two scale, which holds every value to within
+ * 2^-14 of the tile's largest magnitude (a non-finite tile yields NaN).  STORE writes gamma_t * o into acc (the addend of
  * a later ACCUMULATE).  Waits on addend_ready first when it is not NULL. */
 moe_status moe_stage2_accum(const moe_stage_args* a, hipStream_t stream);
 

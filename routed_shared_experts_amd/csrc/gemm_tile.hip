@@ -110,10 +110,40 @@ __device__ __forceinline__ int lds_chunk_off(int r, int c) {
   return (c / 4) * 1024 + (c % 4) * 256 + ((r ^ c ^ ((r & 1) << 3)) & 15) * 16;
 }
 
+// Stage-2 pair rows in 16-bit block-scaled form.  The 64 values v of one
+// (pair, 64-column tile) are stored as codes rint(v * 2^(15 - ex)) with
+// |v| < 2^ex (frexp exponent of the tile's max magnitude), saturated to
+// +-32767, plus the int32 exponent ex: each value is held to within
+// 2^-14 of the tile's max magnitude, at half the bytes of fp32 rows.  The
+// codes fill the first P*H*2 bytes of the pair buffer, the exponents follow
+// ([P][H/64]).  A tile with a non-finite value stores kPairNonFinite.
+constexpr int kPairNonFinite = 0x7FFFFFFF;
+
+__device__ __forceinline__ int16_t* pair_codes(const GemmParams& p) { return reinterpret_cast<int16_t*>(p.pair_out); }
+__device__ __forceinline__ int* pair_exps(const GemmParams& p) {
+  return reinterpret_cast<int*>(reinterpret_cast<char*>(p.pair_out) + (size_t)p.T * p.k_total * p.H * 2);
+}
+__device__ __forceinline__ int pair_tile_exp(float amax) {
+  if (!(amax <= 3.4028234664e38f)) return kPairNonFinite;  // Inf or NaN
+  int ex;
+  (void)__builtin_frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1); 0 for amax = 0
+  return ex;
+}
+// Two values as saturated 16-bit codes in one word (low half first).
+__device__ __forceinline__ uint32_t pair_code2(float a, float b, int ex) {
+  const int sh = 15 - ex;
+  int qa = (int)__builtin_rintf(__builtin_ldexpf(a, sh));
+  int qb = (int)__builtin_rintf(__builtin_ldexpf(b, sh));
+  qa = qa > 32767 ? 32767 : (qa < -32767 ? -32767 : qa);
+  qb = qb > 32767 ? 32767 : (qb < -32767 ? -32767 : qb);
+  return ((uint32_t)qa & 0xFFFFu) | ((uint32_t)qb << 16);
+}
+
 // Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
-// k_total pair rows in slot order, one rounding.  Same arithmetic as
-// last_arrival_sum16, read with ordinary loads: every pair row of the tile was
-// written through this XCD's L2, and each line is read once.
+// k_total pair rows in slot order (each code times its tile's power of two,
+// an exact product, added in fp32), one rounding.  Read with ordinary loads:
+// every pair row of the tile was written through this XCD's L2, and each line
+// is read once.
 __device__ __forceinline__ void last_arrival_sum16_xcd(const GemmParams& p, int tok, int cbase) {
   float v[16];
 #pragma unroll
@@ -125,35 +155,38 @@ __device__ __forceinline__ void last_arrival_sum16_xcd(const GemmParams& p, int 
     v[4 * q + 2] = a.z;
     v[4 * q + 3] = a.w;
   }
-  const float* rows = p.pair_out + (size_t)tok * p.k_total * p.H + cbase;
+  const size_t pair0 = (size_t)tok * p.k_total;
+  const int16_t* rows = pair_codes(p) + pair0 * p.H + cbase;
+  const int* exps = pair_exps(p) + pair0 * (p.H / 64) + cbase / 64;
+  auto add_row = [&](const uint4 (&c)[2], int ex) {
+    const float s = ex == kPairNonFinite ? __builtin_nanf("") : __builtin_ldexpf(1.0f, ex - 15);
+    const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v[2 * q] += (float)(int16_t)(w[q] & 0xFFFFu) * s;
+      v[2 * q + 1] += (float)(int16_t)(w[q] >> 16) * s;
+    }
+  };
   int jj = 0;
   for (; jj + 4 <= p.k_total; jj += 4) {
-    float4 t[4][4];
+    uint4 t[4][2];
+    int ex[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+      const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
+      t[r][0] = src[0];
+      t[r][1] = src[1];
+      ex[r] = exps[(size_t)(jj + r) * (p.H / 64)];
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) t[r][q] = *reinterpret_cast<const float4*>(rows + (size_t)(jj + r) * p.H + 4 * q);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[4 * q] += t[r][q].x;
-        v[4 * q + 1] += t[r][q].y;
-        v[4 * q + 2] += t[r][q].z;
-        v[4 * q + 3] += t[r][q].w;
-      }
+    for (int r = 0; r < 4; ++r) add_row(t[r], ex[r]);
   }
   for (; jj < p.k_total; ++jj) {
-    float4 t[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const float4*>(rows + (size_t)jj * p.H + 4 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[4 * q] += t[q].x;
-      v[4 * q + 1] += t[q].y;
-      v[4 * q + 2] += t[q].z;
-      v[4 * q + 3] += t[q].w;
-    }
+    uint4 t[2];
+    const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H);
+    t[0] = src[0];
+    t[1] = src[1];
+    add_row(t, exps[(size_t)jj * (p.H / 64)]);
   }
   if (p.out_bf16) {
     uint32_t w[8];
@@ -550,39 +583,64 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       }
       return;
     }
-    // ACCUMULATE: the weighted pair rows (64 columns each); the tile's
-    // reduction is XCD-local, so ordinary stores
+    // ACCUMULATE: the weighted pair rows (64 columns each) in the 16-bit
+    // block-scaled form; the tile's reduction is XCD-local, so ordinary stores
+    const int tile_e = c0 / 64;
     if constexpr (k32) {
+      // lanes l and l + 32 hold the tile's 64 columns of token row l % 32
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
         const int r = nn * 32 + lane % 32;
         const int pair = sm.pair[r];
-        if (pair < 0) continue;
         const float sc = sm.rs[r] * ev.wscale;
         const float wgt = sm.rw[r];
-        float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * (lane / 32);
+        float amax = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            acc32[mm][nn][v] = wgt * (acc32[mm][nn][v] * sc);
+            amax = fmaxf(amax, fabsf(acc32[mm][nn][v]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        if (pair < 0) continue;
+        const int ex = pair_tile_exp(amax);
+        int16_t* dst = pair_codes(p) + (size_t)pair * p.H + c0 + 4 * (lane / 32);
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4*>(dst + 32 * mm + 8 * j) =
-                make_float4(wgt * (acc32[mm][nn][4 * j] * sc), wgt * (acc32[mm][nn][4 * j + 1] * sc),
-                            wgt * (acc32[mm][nn][4 * j + 2] * sc), wgt * (acc32[mm][nn][4 * j + 3] * sc));
+            *reinterpret_cast<uint2*>(dst + 32 * mm + 8 * j) =
+                make_uint2(pair_code2(acc32[mm][nn][4 * j], acc32[mm][nn][4 * j + 1], ex),
+                           pair_code2(acc32[mm][nn][4 * j + 2], acc32[mm][nn][4 * j + 3], ex));
+        if (lane < 32) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
       }
     } else {
+      // lanes (g, l16), g = 0..3, hold the tile's 64 columns of token row l16
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int r = nb * 16 + l16;
         const int pair = sm.pair[r];
-        if (pair < 0) continue;
         const float sc = sm.rs[r] * ev.wscale;
         const float wgt = sm.rw[r];
-        float* dst = p.pair_out + (size_t)pair * p.H + c0 + 4 * g;
+        float amax = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          *reinterpret_cast<float4*>(dst + mb * 16) =
-              make_float4(wgt * (acc[mb][nb][0] * sc), wgt * (acc[mb][nb][1] * sc), wgt * (acc[mb][nb][2] * sc),
-                          wgt * (acc[mb][nb][3] * sc));
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc[mb][nb][v] = wgt * (acc[mb][nb][v] * sc);
+            amax = fmaxf(amax, fabsf(acc[mb][nb][v]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        if (pair < 0) continue;
+        const int ex = pair_tile_exp(amax);
+        int16_t* dst = pair_codes(p) + (size_t)pair * p.H + c0 + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          *reinterpret_cast<uint2*>(dst + mb * 16) = make_uint2(pair_code2(acc[mb][nb][0], acc[mb][nb][1], ex),
+                                                                pair_code2(acc[mb][nb][2], acc[mb][nb][3], ex));
+        if (g == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
       }
     }
     // count arrivals once the stores have reached the L2 (their acknowledgement);
