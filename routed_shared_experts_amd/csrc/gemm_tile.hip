@@ -80,15 +80,54 @@ __device__ __forceinline__ uint4 tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
 // column tile by column tile, the blocks of one column tile side by side, so
 // the concurrent workgroups of an expert share each weight tile through L2
 // instead of streaming the expert's weights once per block.  In: the item
-// index `it` of block-major order; out: block b and column tile c.
+// index `it` of block-major order; out: block b and column tile c; returns
+// the expert.
 __device__ __forceinline__ int split_of(const GemmParams& p) { return p.bsplit > 1 ? p.bsplit : 1; }
 
-__device__ __forceinline__ void expert_major(const GemmParams& p, int BM, int n_per, int it, int& b, int& c) {
+__device__ __forceinline__ int expert_major(const GemmParams& p, int BM, int n_per, int it, int& b, int& c) {
   const int e = p.block_expert[it / n_per / split_of(p)];
   const int bs = p.offsets[e] / BM, nb = (p.offsets[e + 1] - p.offsets[e]) / BM;
   const int local = it - bs * n_per;
   c = local / nb;
   b = bs + local % nb;
+  return e;
+}
+
+// Row tables of block b: the token and pair of each row go to LDS; the
+// row's epilogue factors (stage-2 pair weight, A8W8 row scale) stay in the
+// loading thread's registers (tid < BM) until the epilogue, so no load of
+// the K loop waits behind them.
+template <int FMT, int STAGE, int BM>
+__device__ __forceinline__ void tile_rows(const GemmParams& p, int b, int tid, int* s_tok, int* s_pair, float& rw,
+                                          float& rs) {
+  const int P = p.T * p.k_total;
+  rw = 0.f;
+  rs = 1.0f;
+  if (tid < BM) {
+    const int slot = b * BM + tid;
+    int tok = -1, pair = -1;
+    if (p.dense) {
+      tok = slot < p.T ? slot : -1;
+    } else {
+      pair = p.sorted[slot];
+      if (pair < P) {
+        tok = pair / p.k_total;
+        if (STAGE == 2) rw = p.pair_w[pair];
+      } else {
+        pair = -1;
+      }
+    }
+    s_tok[tid] = tok;
+    s_pair[tid] = pair;
+    if (FMT == FMT_A8W8) {
+      if (STAGE == 1) {
+        rs = tok >= 0 ? static_cast<const float*>(p.x_s)[tok] : 0.f;
+      } else {
+        const float amax = static_cast<const float*>(p.h_s)[slot];
+        if (amax > 0.f) rs = __fdiv_rn(amax, 448.0f);
+      }
+    }
+  }
 }
 
 template <int BM>
@@ -222,9 +261,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   const int lane = tid % kWave;
   const int g = lane / 16, l16 = lane % 16;
 
-  setup_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, sm.rw, sm.rs);
-  __syncthreads();
-
   // K extent in bytes of the staged (MFMA) format; a multiple of 128
   const int kbytes = (STAGE == 1) ? p.H * esz : ev.width * esz;
   const int nk = kbytes / 128;
@@ -271,24 +307,27 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // LDS offset of chunk u: row tid / 8 + 32 u sits two 16-row fragments
   // (4 KiB) further on per u, with the same swizzle
   const uint32_t soff = (uint32_t)(lds_chunk_off((tid / 8) % 16, tid % 8) + (tid / 128) * 2048);
+  // buffer offsets of the thread's chunks (set once the row tables are in LDS)
   uint32_t xoff[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const int q = tid + kTileThreads * u;
-    const int r = q / 8;
-    const int c = q % 8;  // 16-byte chunk of the 128-byte K tile
-    const int tok = sm.tok[r];
-    if (tok < 0) {
-      xoff[u] = kTileOutOfRange;
-    } else if (STAGE == 1) {
-      xoff[u] = (uint32_t)((size_t)tok * p.H * esz) + c * 16;
-    } else {
-      xoff[u] = (uint32_t)(((size_t)b * BM + r) * h_row_bytes<FMT>(p)) + c * 16;
-    }
-  }
   uint32_t xsoff = kTileOutOfRange;  // the row's e8m0 scales (MX), for threads tid < BM
-  if (FMT == FMT_MX && tid < BM && sm.tok[tid] >= 0)
-    xsoff = (STAGE == 1) ? (uint32_t)(sm.tok[tid] * (p.H / 32)) : (uint32_t)((b * BM + tid) * (p.ld_h / 32));
+  auto row_offsets = [&]() {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + kTileThreads * u;
+      const int r = q / 8;
+      const int c = q % 8;  // 16-byte chunk of the 128-byte K tile
+      const int tok = sm.tok[r];
+      if (tok < 0) {
+        xoff[u] = kTileOutOfRange;
+      } else if (STAGE == 1) {
+        xoff[u] = (uint32_t)((size_t)tok * p.H * esz) + c * 16;
+      } else {
+        xoff[u] = (uint32_t)(((size_t)b * BM + r) * h_row_bytes<FMT>(p)) + c * 16;
+      }
+    }
+    if (FMT == FMT_MX && tid < BM && sm.tok[tid] >= 0)
+      xsoff = (STAGE == 1) ? (uint32_t)(sm.tok[tid] * (p.H / 32)) : (uint32_t)((b * BM + tid) * (p.ld_h / 32));
+  };
 
   auto load_w = [&](uint4 (&w)[4][2], int (&sc)[4], int kt) {
     kt = kt < nk ? kt : nk - 1;  // past the end: a harmless reload of the last tile
@@ -427,22 +466,24 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // (XD = 2, register set = tile parity) are loading; after the multiply the
   // rows of kt + 1 are staged into the other LDS buffer.  Every step is
   // unconditional; loads past the end reload the last tile.
-  // The prologue issues its loads in the order the loop keeps in flight
-  // (rows kt + 1, weights kt, rows kt + 2, weights kt + 1): the wait counts
-  // the compiler derives at the loop head hold for the first pass too, so
-  // staging a tile never waits for loads issued after it.
+  // The weights of the first two K tiles depend only on the expert and the
+  // columns, so they are in flight before the row tables are read; the
+  // token rows follow once the tables are in LDS.
   uint4 wA[4][2], wB[4][2];
   int sA[4], sB[4];
+  load_w(wA, sA, 0);
+  load_w(wB, sB, 1);
+  float rw_row, rs_row;
+  tile_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, rw_row, rs_row);
+  __syncthreads();
+  if (sm.tok[0] < 0) return;  // a block part holding only padding rows (padding sits at the end)
+  row_offsets();
   if constexpr (XD == 2) {
     load_x(0, 0);
     load_x(1, 1);
-    load_w(wA, sA, 0);
     store_x(0, 0);
     load_x(0, 2);
-    load_w(wB, sB, 1);
   } else {
-    load_w(wA, sA, 0);
-    load_w(wB, sB, 1);
     load_x(0, 0);
     store_x(0, 0);
   }
@@ -463,6 +504,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     __syncthreads();
   }
   if (kt < nk) compute(0, wA, sA);  // odd tile count: the last tile sits in buffer 0 / set A
+  if (tid < BM) {
+    sm.rw[tid] = rw_row;
+    sm.rs[tid] = rs_row;
+  }
+  __syncthreads();
 
   // ---- epilogues (per wave, from registers) ----
   // acc[mb][nb][v] = row (mb, 4g + v) of the wave's weight rows x token row nb*16 + l16
@@ -733,10 +779,11 @@ void gemm_tile_kernel(GemmParams p) {
   if ((int)blockIdx.x >= active) return;
   const int lt = (STAGE == 1) ? xcd_remap((int)blockIdx.x, active) : (int)blockIdx.x;
   int b = lt / n_col, nc = lt % n_col;
-  if (STAGE == 1 && !p.dense && p.offsets) expert_major(p, BM, n_col, lt, b, nc);
+  int e = -1;
+  if (STAGE == 1 && !p.dense && p.offsets) e = expert_major(p, BM, n_col, lt, b, nc);
+  else if (!p.dense) e = p.block_expert[b];
   const int n0 = nc * WCOLS;
 
-  const int e = p.dense ? -1 : p.block_expert[b];
   const ExpertView ev = resolve_expert<FMT, STAGE>(p, e);
   if (STAGE == 1 && n0 >= ev.width) return;  // past a narrow pseudo-expert chunk (uniform)
   int c0 = n0 + wv * ((STAGE == 1) ? 32 : 64);
@@ -760,7 +807,6 @@ void gemm_tile_accum_kernel(GemmParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n64 = p.H / 64;
   const int nblk = *p.num_blocks * split_of(p);
-  const int P = p.T * p.k_total;
   int* q_next = p.counters + (size_t)p.T * n64;
   int* q_owner = q_next + kNumXcd;
   const int me = xcc_id();
@@ -787,13 +833,10 @@ void gemm_tile_accum_kernel(GemmParams p) {
       __syncthreads();
       if (it >= items_q) break;
       int b = it / groups_q, j = it % groups_q;
-      if (p.offsets) expert_major(p, BM, groups_q, it, b, j);
+      const int e = p.offsets ? expert_major(p, BM, groups_q, it, b, j) : p.block_expert[b / split_of(p)];
       const int t = q + kNumXcd * (4 * j + wv);
       const bool wave_ok = t < n64;
-      // split blocks: a part holding only padding rows has nothing to do
-      // (padding sits at the end of an expert's rows)
-      if (split_of(p) > 1 && p.sorted[(size_t)b * BM] >= P) continue;
-      const ExpertView ev = resolve_expert<FMT, 2>(p, p.block_expert[b / split_of(p)]);
+      const ExpertView ev = resolve_expert<FMT, 2>(p, e);
       tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok);
       __syncthreads();  // the next item rewrites the row tables
     }
