@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "a8w8": 5000.0}
 DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "a8w8": "fp8-e4m3"}
 TIMING_EVERY = 8
+N_EVENTS = 7  # timing events the layer takes (prologue and sort spans, each GEMM kernel's start and end)
 # sources of the GEMM kernels: the stage-1 traffic figure in profiles/ holds
 # only while their hash is the one it was measured with
 KERNEL_SOURCES = ["gemm_wave.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"]
@@ -166,7 +167,7 @@ def main():
         out = layers[0].out
         for L in layers[1:]:
             L.args.out = m._ptr(out)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(N_EVENTS)] for _ in range(args.steps)]
         stream = torch.cuda.current_stream()
         for e in evs:
             for x in e:
@@ -191,9 +192,10 @@ def main():
             el = time.perf_counter() - t0
             stage = None
         else:
-            # live per-kernel timing: events between the layer's launches on the
-            # main stream, on every TIMING_EVERY-th step
-            handles = [m.ctypes.cast((m.c_void_p * 5)(*[x.cuda_event for x in e]), m.c_void_p) for e in evs]
+            # live per-kernel timing on every TIMING_EVERY-th step: events
+            # between the prologue launches on the main stream, and events
+            # stamped with each GEMM kernel's own start and end
+            handles = [m.ctypes.cast((m.c_void_p * N_EVENTS)(*[x.cuda_event for x in e]), m.c_void_p) for e in evs]
             timed = [i for i in range(args.steps) if i % TIMING_EVERY == 0]
             t0 = time.perf_counter()
             for i in range(args.steps):
@@ -204,9 +206,9 @@ def main():
             el = time.perf_counter() - t0
             for L in layers:
                 L.args.timing_events = None
-            names = ["prologue", "sort", "stage1", "stage2"]
-            stage = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in timed]))
-                     for j, n in enumerate(names)}
+            spans = {"prologue": (0, 1), "sort": (1, 2), "stage1": (3, 4), "stage2": (5, 6)}
+            stage = {n: float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in timed]))
+                     for n, (a, b) in spans.items()}
         results[mode] = (el, stage, layers[0])
         del layers
 

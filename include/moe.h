@@ -156,9 +156,11 @@ typedef struct {
   /* output */
   void* out;         /* [T][H] */
   int32_t out_dtype; /* F32 or BF16 */
-  /* optional instrumentation: NULL, or 5 caller-created events recorded on the
-   * main stream before the prologue, after the prologue, after the sort, after
-   * routed stage 1 and after routed stage 2 (for live per-kernel timing) */
+  /* optional instrumentation: NULL, or 7 caller-created timing events: [0]
+   * before the prologue, [1] after the prologue, [2] after the sort (recorded
+   * on the main stream), [3]/[4] the start/end of the routed stage-1 GEMM
+   * kernel and [5]/[6] those of the routed stage-2 GEMM kernel (stamped by
+   * the kernels' own dispatch) */
   hipEvent_t* timing_events;
 } moe_forward_args;
 

@@ -659,8 +659,11 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.ld_h = a->I;
   g.h_s = fmt == FMT_MX ? static_cast<void*>(ws + pl.off_hs)
                         : (fmt == FMT_A8W8 ? static_cast<void*>(ws + pl.off_amax) : nullptr);
+  if (tev) {
+    g.ev_start = tev[3];
+    g.ev_stop = tev[4];
+  }
   HIP_TRY(launch_gemm(g, 1, fmt, 64, main_s));
-  if (tev) HIP_TRY(hipEventRecord(tev[3], main_s));
 
   // 5. routed stage 2: weighted scatter-add onto the addend, last arrival writes out
   if (aux) HIP_TRY(hipStreamWaitEvent(main_s, ev_ready, 0));
@@ -668,8 +671,11 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.mode = MOE_STAGE2_ACCUMULATE;
   g.counters = cnt;
   g.expected = pl.k_total;
+  if (tev) {
+    g.ev_start = tev[5];
+    g.ev_stop = tev[6];
+  }
   HIP_TRY(launch_gemm(g, 2, fmt, 64, main_s));
-  if (tev) HIP_TRY(hipEventRecord(tev[4], main_s));
   return MOE_OK;
 }
 

@@ -296,8 +296,7 @@ static hipError_t launch_bm(const GemmParams& p, int bn, hipStream_t s) {
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const int n_tiles = (width_max + BN - 1) / BN;
   dim3 grid((unsigned)(p.max_blocks * n_tiles));
-  hipLaunchKernelGGL((gemm_kernel<FMT, STAGE, BM, BN>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_gemm_kernel(gemm_kernel<FMT, STAGE, BM, BN>, grid, dim3(256), s, p);
 }
 
 template <int FMT, int STAGE>

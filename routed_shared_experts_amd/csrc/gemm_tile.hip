@@ -871,15 +871,13 @@ static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
     const int groups = ((n64 + kNumXcd - 1) / kNumXcd + 3) / 4;
     long long per_xcd = (long long)p.max_blocks * groups;
     if (per_xcd > 64) per_xcd = 64;
-    hipLaunchKernelGGL((gemm_tile_accum_kernel<FMT, NB>), dim3((unsigned)(kNumXcd * per_xcd)), dim3(kTileThreads), 0, s,
-                       p);
-    return hipGetLastError();
+    return launch_gemm_kernel(gemm_tile_accum_kernel<FMT, NB>, dim3((unsigned)(kNumXcd * per_xcd)),
+                              dim3(kTileThreads), s, p);
   }
   constexpr int WCOLS = (STAGE == 1) ? 128 : 256;
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const dim3 grid((unsigned)(p.max_blocks * (width_max / WCOLS)));
-  hipLaunchKernelGGL((gemm_tile_kernel<FMT, STAGE, NB>), grid, dim3(kTileThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_gemm_kernel(gemm_tile_kernel<FMT, STAGE, NB>, grid, dim3(kTileThreads), s, p);
 }
 
 template <int FMT, int STAGE>

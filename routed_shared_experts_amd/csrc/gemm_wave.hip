@@ -401,11 +401,8 @@ static hipError_t launch_wv(const GemmParams& p, int depth, hipStream_t s) {
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const long long route_wgs = (STAGE == 1 && p.route_fused) ? p.route.T + clear_blocks(p.route.zero_vec, 64) : 0;
   const dim3 grid((unsigned)(p.max_blocks * (width_max / CW) + route_wgs));
-  if (depth >= 2)
-    hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 2>), grid, dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_wave_kernel<FMT, STAGE, 1>), grid, dim3(64), 0, s, p);
-  return hipGetLastError();
+  if (depth >= 2) return launch_gemm_kernel(gemm_wave_kernel<FMT, STAGE, 2>, grid, dim3(64), s, p);
+  return launch_gemm_kernel(gemm_wave_kernel<FMT, STAGE, 1>, grid, dim3(64), s, p);
 }
 
 // Activation buffers are addressed with 32-bit buffer offsets; widths must

@@ -2,6 +2,7 @@
 // gfx950 kernels.  Not part of the public C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -92,7 +93,21 @@ struct GemmParams {
   // route.zero_ptr
   int route_fused;
   RouteParams route;
+  // host side only: events stamped with the GEMM kernel's own start and end
+  // (instrumentation; both NULL for an ordinary launch)
+  hipEvent_t ev_start, ev_stop;
 };
+
+// Launch of a GEMM kernel taking GemmParams; with instrumentation events the
+// dispatch itself records the kernel's start and end times on them.
+template <typename K>
+inline hipError_t launch_gemm_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, const GemmParams& p) {
+  if (p.ev_start || p.ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, p.ev_start, p.ev_stop, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_gate_dot(const void* x, int x_f32, const void* g, int T, int H, int apply_sigmoid,
