@@ -358,7 +358,10 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   // token-row register sets in flight: XD = 2 keeps the rows of K tiles
   // kt + 1 and kt + 2 loading while tile kt is multiplied
-  constexpr int XD = ((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) ? 1 : 2;
+  constexpr int XD =
+      (((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) || (FMT == FMT_A8W8 && STAGE == 2 && NB == 4))
+          ? 1
+          : 2;
   uint4 xr[XD][CPT];
   uint32_t xsr[XD] = {};
   auto load_x = [&](int set, int kt) {
@@ -753,11 +756,13 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   }
 }
 
-// Waves per SIMD the register allocation targets: two workgroups per CU keep
-// twice the loads in flight, where the operand registers allow it without
-// spilling much (bf16; 32- and 64-row blocks; 128-row a8w8 stage 1).
+// Waves per SIMD the register allocation targets: two or three workgroups per
+// CU keep more loads in flight, where the operand registers allow it without
+// spilling much (bf16; 32- and 64-row blocks; 128-row a8w8 stage 1; three
+// for the 64-row a8w8 stage-2 items).
 template <int FMT, int STAGE, int NB>
 constexpr int tile_waves_per_eu() {
+  if (FMT == FMT_A8W8 && STAGE == 2 && NB == 4) return 3;  // with one token-row set in flight (a8w8 stage 2 -2 %)
   return (FMT == FMT_BF16 || NB <= 4 || (FMT == FMT_A8W8 && STAGE == 1)) ? 2 : 1;
 }
 
@@ -865,12 +870,13 @@ bool tile_kernel_fits(const GemmParams& p, int stage, int fmt) {
 template <int FMT, int STAGE, int NB>
 static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
   if (STAGE == 2 && p.mode != 0) {
-    // persistent: two workgroups per CU of each XCD at most (an XCD has 32
-    // CUs), no more than the largest queue has items
+    // persistent: as many workgroups per CU of each XCD as the register
+    // allocation allows (an XCD has 32 CUs), no more than the largest queue
+    // has items
     const int n64 = p.H / 64;
     const int groups = ((n64 + kNumXcd - 1) / kNumXcd + 3) / 4;
     long long per_xcd = (long long)p.max_blocks * groups;
-    if (per_xcd > 64) per_xcd = 64;
+    if (per_xcd > 32 * tile_waves_per_eu<FMT, 2, NB>()) per_xcd = 32 * tile_waves_per_eu<FMT, 2, NB>();
     return launch_gemm_kernel(gemm_tile_accum_kernel<FMT, NB>, dim3((unsigned)(kNumXcd * per_xcd)),
                               dim3(kTileThreads), s, p);
   }
