@@ -132,7 +132,9 @@ __device__ __forceinline__ void tile_rows(const GemmParams& p, int b, int tid, i
 
 template <int BM>
 struct TileSmem {
-  uint8_t x[2][BM * 128];  // staged token rows, swizzled operand order
+  // staged token rows, swizzled operand order; after the K loop each wave's
+  // 4 KiB of it stages the stage-2 pair-row codes of 32 rows
+  uint8_t x[2][(BM < 64 ? 64 : BM) * 128];
   uint32_t xsc[2][BM + 1];  // MX: the rows' e8m0 scales of the staged K tile, + a spare slot
   int tok[BM];
   int pair[BM];
@@ -635,11 +637,32 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     // ACCUMULATE: the weighted pair rows (64 columns each) in the 16-bit
     // block-scaled form; the tile's reduction is XCD-local, so ordinary stores
     const int tile_e = c0 / 64;
+    // Each (pair, tile) is one 128-byte line of codes.  The codes pass through
+    // this wave's 4 KiB of the idle staging buffer (16-byte chunk c of row r
+    // at r * 128 + 16 (c ^ (r & 7))) so that eight lanes store a row's line
+    // whole, eight rows per instruction.
+    uint8_t* wl = &sm.x[0][0] + (tid / kWave) * 4096;
+    auto store_rows = [&](int r0, int nrows) {  // rows r0 .. r0 + nrows - 1 of the block, staged at wl
+      wave_lds_sync();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = lane / 8 + 8 * k;
+        const int c = lane % 8;
+        if (rr < nrows) {
+          const uint4 v = *reinterpret_cast<const uint4*>(wl + rr * 128 + 16 * (c ^ (rr & 7)));
+          const int pr = sm.pair[r0 + rr];
+          if (pr >= 0) *reinterpret_cast<uint4*>(pair_codes(p) + (size_t)pr * p.H + c0 + 8 * c) = v;
+        }
+      }
+      wave_lds_sync();  // the next group rewrites the region
+    };
     if constexpr (k32) {
-      // lanes l and l + 32 hold the tile's 64 columns of token row l % 32
+      // lanes l and l + 32 hold the tile's 64 columns of token row l % 32 of
+      // each 32-row group (columns 32 mm + 8 j + 4 (l / 32) + 0..3)
+      const int rl = lane % 32, h = lane / 32;
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
-        const int r = nn * 32 + lane % 32;
+        const int r = nn * 32 + rl;
         const int pair = sm.pair[r];
         const float sc = sm.rs[r] * ev.wscale;
         const float wgt = sm.rw[r];
@@ -652,20 +675,20 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
             amax = fmaxf(amax, fabsf(acc32[mm][nn][v]));
           }
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        if (pair < 0) continue;
         const int ex = pair_tile_exp(amax);
-        int16_t* dst = pair_codes(p) + (size_t)pair * p.H + c0 + 4 * (lane / 32);
+        if (pair >= 0 && h == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<uint2*>(dst + 32 * mm + 8 * j) =
+            *reinterpret_cast<uint2*>(wl + rl * 128 + 16 * ((4 * mm + j) ^ (rl & 7)) + 8 * h) =
                 make_uint2(pair_code2(acc32[mm][nn][4 * j], acc32[mm][nn][4 * j + 1], ex),
                            pair_code2(acc32[mm][nn][4 * j + 2], acc32[mm][nn][4 * j + 3], ex));
-        if (lane < 32) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
+        store_rows(nn * 32, 32);
       }
     } else {
       // lanes (g, l16), g = 0..3, hold the tile's 64 columns of token row l16
+      // of each 16-row group (columns 16 mb + 4 g + 0..3)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int r = nb * 16 + l16;
@@ -682,14 +705,14 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        if (pair < 0) continue;
         const int ex = pair_tile_exp(amax);
-        int16_t* dst = pair_codes(p) + (size_t)pair * p.H + c0 + 4 * g;
+        if (pair >= 0 && g == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          *reinterpret_cast<uint2*>(dst + mb * 16) = make_uint2(pair_code2(acc[mb][nb][0], acc[mb][nb][1], ex),
-                                                                pair_code2(acc[mb][nb][2], acc[mb][nb][3], ex));
-        if (g == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
+          *reinterpret_cast<uint2*>(wl + l16 * 128 + 16 * ((2 * mb + g / 2) ^ (l16 & 7)) + 8 * (g % 2)) =
+              make_uint2(pair_code2(acc[mb][nb][0], acc[mb][nb][1], ex),
+                         pair_code2(acc[mb][nb][2], acc[mb][nb][3], ex));
+        store_rows(nb * 16, 16);
       }
     }
     // count arrivals once the stores have reached the L2 (their acknowledgement);
