@@ -182,64 +182,57 @@ __device__ __forceinline__ uint32_t pair_code2(float a, float b, int ex) {
 
 // Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
 // k_total pair rows in slot order (each code times its tile's power of two,
-// an exact product, added in fp32), one rounding.  Read with ordinary loads:
-// every pair row of the tile was written through this XCD's L2, and each line
-// is read once.
-__device__ __forceinline__ void last_arrival_sum16_xcd(const GemmParams& p, int tok, int cbase) {
-  float v[16];
+// an exact product, added in fp32), one rounding.  Eight lanes share a token
+// (lane part c sums columns cbase + 8c .. + 7), so each load of a row of
+// codes reads its 128-byte line whole.  Read with ordinary loads: every pair
+// row of the tile was written through this XCD's L2.
+__device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int tok, int cbase, int c) {
+  const int col = cbase + 8 * c;
+  float v[8];
+  if (p.acc) {
+    const float4 a0 = *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + col);
+    const float4 a1 = *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + col + 4);
+    v[0] = a0.x, v[1] = a0.y, v[2] = a0.z, v[3] = a0.w;
+    v[4] = a1.x, v[5] = a1.y, v[6] = a1.z, v[7] = a1.w;
+  } else {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 a = p.acc ? *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + cbase + 4 * q)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-    v[4 * q] = a.x;
-    v[4 * q + 1] = a.y;
-    v[4 * q + 2] = a.z;
-    v[4 * q + 3] = a.w;
+    for (int q = 0; q < 8; ++q) v[q] = 0.f;
   }
   const size_t pair0 = (size_t)tok * p.k_total;
-  const int16_t* rows = pair_codes(p) + pair0 * p.H + cbase;
+  const int16_t* rows = pair_codes(p) + pair0 * p.H + col;
   const int* exps = pair_exps(p) + pair0 * (p.H / 64) + cbase / 64;
-  auto add_row = [&](const uint4 (&c)[2], int ex) {
+  auto add_row = [&](const uint4& t, int ex) {
     const float s = ex == kPairNonFinite ? __builtin_nanf("") : __builtin_ldexpf(1.0f, ex - 15);
-    const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       v[2 * q] += (float)(int16_t)(w[q] & 0xFFFFu) * s;
       v[2 * q + 1] += (float)(int16_t)(w[q] >> 16) * s;
     }
   };
   int jj = 0;
   for (; jj + 4 <= p.k_total; jj += 4) {
-    uint4 t[4][2];
+    uint4 t[4];
     int ex[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
-      t[r][0] = src[0];
-      t[r][1] = src[1];
+      t[r] = *reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
       ex[r] = exps[(size_t)(jj + r) * (p.H / 64)];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) add_row(t[r], ex[r]);
   }
-  for (; jj < p.k_total; ++jj) {
-    uint4 t[2];
-    const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H);
-    t[0] = src[0];
-    t[1] = src[1];
-    add_row(t, exps[(size_t)jj * (p.H / 64)]);
-  }
+  for (; jj < p.k_total; ++jj)
+    add_row(*reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H), exps[(size_t)jj * (p.H / 64)]);
   if (p.out_bf16) {
-    uint32_t w[8];
+    uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
-    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok * p.H + cbase);
-    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int q = 0; q < 4; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok * p.H + col) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok * p.H + cbase);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok * p.H + col);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
 }
 
@@ -754,11 +747,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) total += __popc(cnt[nb]);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // the wave's last arrivals, compacted 16 at a time: entry i -> lanes
-    // (g, i % 16), each summing 16 of the tile's 64 columns
+    // the wave's last arrivals, compacted 8 at a time: entry i -> lanes
+    // 8 (i % 8) .. + 7, each summing 8 of the tile's 64 columns
     if (total > 0) {
-      for (int base = 0; base < total; base += 16) {
-        const int i = base + l16;
+      for (int base = 0; base < total; base += 8) {
+        const int i = base + lane / 8;
         if (i < total) {
           // the i-th done slot in (row block, token) order
           int rem = i, r = -1;
@@ -772,7 +765,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
             }
             if (r < 0) rem -= c;
           }
-          last_arrival_sum16_xcd(p, sm.tok[r], c0 + 16 * g);
+          last_arrival_sum8_xcd(p, sm.tok[r], c0, lane % 8);
         }
       }
     }
