@@ -352,8 +352,9 @@ moe_status moe_stage1(const moe_stage_args* a, hipStream_t stream);
  * once into out (deterministic: the result does not depend on the order in
  * which workgroups finish).  The one-wave kernels (16-row blocks) keep the
  * rows in fp32; the 32-128-row kernels store each (pair, 64-column tile) as
- * 16-bit codes with one power-of-two scale, which holds every value to within
- * 2^-14 of the tile's largest magnitude (a non-finite tile yields NaN).  STORE writes gamma_t * o into acc (the addend of
+ * one 128-byte line of 16-bit words carrying 15-bit values and the tile's
+ * power-of-two scale, which holds every value to within 2^-13 of the tile's
+ * largest magnitude (a non-finite tile yields NaN).  STORE writes gamma_t * o into acc (the addend of
  * a later ACCUMULATE).  Waits on addend_ready first when it is not NULL. */
 moe_status moe_stage2_accum(const moe_stage_args* a, hipStream_t stream);
 

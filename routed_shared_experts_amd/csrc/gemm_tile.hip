@@ -152,41 +152,45 @@ __device__ __forceinline__ int lds_chunk_off(int r, int c) {
 }
 
 // Stage-2 pair rows in 16-bit block-scaled form.  The 64 values v of one
-// (pair, 64-column tile) are stored as codes rint(v * 2^(15 - ex)) with
-// |v| < 2^ex (frexp exponent of the tile's max magnitude), saturated to
-// +-32767, plus the int32 exponent ex: each value is held to within
-// 2^-14 of the tile's max magnitude, at half the bytes of fp32 rows.  The
-// codes fill the first P*H*2 bytes of the pair buffer, the exponents follow
-// ([P][H/64]).  A tile with a non-finite value stores kPairNonFinite.
-constexpr int kPairNonFinite = 0x7FFFFFFF;
+// (pair, 64-column tile) become one 128-byte line of 16-bit words
+// 2 q + b: q = rint(v * 2^(14 - e)) saturated to +-16383, with e the frexp
+// exponent of the tile's largest magnitude (|v| < 2^e) raised to at least
+// -126, and b, the lowest bit of the words of columns 0..7, spelling the
+// 8-bit field e + 126 (255: the tile holds a non-finite value).  Each value
+// is held to within 2^-13 of the tile's largest magnitude, at half the bytes
+// of fp32, and every line is written once and read once, so no cache ever
+// holds a stale copy of it.  The words fill the first P*H*2 bytes of the pair
+// buffer.
+constexpr int kPairNonFinite = 255;
 
 __device__ __forceinline__ int16_t* pair_codes(const GemmParams& p) { return reinterpret_cast<int16_t*>(p.pair_out); }
-__device__ __forceinline__ int* pair_exps(const GemmParams& p) {
-  return reinterpret_cast<int*>(reinterpret_cast<char*>(p.pair_out) + (size_t)p.T * p.k_total * p.H * 2);
-}
-__device__ __forceinline__ int pair_tile_exp(float amax) {
+// The tile's 8-bit exponent field from its largest magnitude.
+__device__ __forceinline__ int pair_tile_field(float amax) {
   if (!(amax <= 3.4028234664e38f)) return kPairNonFinite;  // Inf or NaN
   int ex;
   (void)__builtin_frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1); 0 for amax = 0
-  return ex;
+  return (ex < -126 ? -126 : ex) + 126;
 }
-// Two values as saturated 16-bit codes in one word (low half first).
-__device__ __forceinline__ uint32_t pair_code2(float a, float b, int ex) {
-  const int sh = 15 - ex;
+// Words of two values of columns col, col + 1 of the tile (low half first).
+__device__ __forceinline__ uint32_t pair_code2(float a, float b, int field, int col) {
+  const int sh = 14 - ((field == kPairNonFinite ? 0 : field) - 126);
   int qa = (int)__builtin_rintf(__builtin_ldexpf(a, sh));
   int qb = (int)__builtin_rintf(__builtin_ldexpf(b, sh));
-  qa = qa > 32767 ? 32767 : (qa < -32767 ? -32767 : qa);
-  qb = qb > 32767 ? 32767 : (qb < -32767 ? -32767 : qb);
-  return ((uint32_t)qa & 0xFFFFu) | ((uint32_t)qb << 16);
+  qa = qa > 16383 ? 16383 : (qa < -16383 ? -16383 : qa);
+  qb = qb > 16383 ? 16383 : (qb < -16383 ? -16383 : qb);
+  const int ba = col < 8 ? (field >> col) & 1 : 0;
+  const int bb = col + 1 < 8 ? (field >> (col + 1)) & 1 : 0;
+  return ((uint32_t)(2 * qa + ba) & 0xFFFFu) | ((uint32_t)(2 * qb + bb) << 16);
 }
 
 // Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
-// k_total pair rows in slot order (each code times its tile's power of two,
-// an exact product, added in fp32), one rounding.  Eight lanes share a token
-// (lane part c sums columns cbase + 8c .. + 7), so each load of a row of
-// codes reads its 128-byte line whole.  Read with ordinary loads: every pair
-// row of the tile was written through this XCD's L2.
-__device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int tok, int cbase, int c) {
+// k_total pair rows in slot order (each q times its tile's power of two, an
+// exact product, added in fp32), one rounding.  Eight lanes share a token
+// (lane part c sums columns cbase + 8c .. + 7), so each load of a row reads
+// its 128-byte line whole; part 0 holds the exponent bits and passes the
+// field to the other seven.  Read with ordinary loads: every pair row of the
+// tile was written through this XCD's L2.
+__device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int tok, int cbase, int c, int lane) {
   const int col = cbase + 8 * c;
   float v[8];
   if (p.acc) {
@@ -198,32 +202,30 @@ __device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int t
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
   }
-  const size_t pair0 = (size_t)tok * p.k_total;
-  const int16_t* rows = pair_codes(p) + pair0 * p.H + col;
-  const int* exps = pair_exps(p) + pair0 * (p.H / 64) + cbase / 64;
-  auto add_row = [&](const uint4& t, int ex) {
-    const float s = ex == kPairNonFinite ? __builtin_nanf("") : __builtin_ldexpf(1.0f, ex - 15);
+  const int16_t* rows = pair_codes(p) + (size_t)tok * p.k_total * p.H + col;
+  const int src = lane & ~7;  // part 0 of this token
+  auto add_row = [&](const uint4& t) {
     const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+    int field = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) field |= (int)((w[q] & 1u) << (2 * q)) | (int)(((w[q] >> 16) & 1u) << (2 * q + 1));
+    field = __shfl(field, src, kWave);
+    const float s = field == kPairNonFinite ? __builtin_nanf("") : __builtin_ldexpf(1.0f, field - 126 - 14);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v[2 * q] += (float)(int16_t)(w[q] & 0xFFFFu) * s;
-      v[2 * q + 1] += (float)(int16_t)(w[q] >> 16) * s;
+      v[2 * q] += (float)((int)(int16_t)(w[q] & 0xFFFFu) >> 1) * s;
+      v[2 * q + 1] += (float)((int)(int16_t)(w[q] >> 16) >> 1) * s;
     }
   };
   int jj = 0;
   for (; jj + 4 <= p.k_total; jj += 4) {
     uint4 t[4];
-    int ex[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      t[r] = *reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
-      ex[r] = exps[(size_t)(jj + r) * (p.H / 64)];
-    }
+    for (int r = 0; r < 4; ++r) t[r] = *reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) add_row(t[r], ex[r]);
+    for (int r = 0; r < 4; ++r) add_row(t[r]);
   }
-  for (; jj < p.k_total; ++jj)
-    add_row(*reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H), exps[(size_t)jj * (p.H / 64)]);
+  for (; jj < p.k_total; ++jj) add_row(*reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H));
   if (p.out_bf16) {
     uint32_t w[4];
 #pragma unroll
@@ -629,7 +631,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     }
     // ACCUMULATE: the weighted pair rows (64 columns each) in the 16-bit
     // block-scaled form; the tile's reduction is XCD-local, so ordinary stores
-    const int tile_e = c0 / 64;
     // Each (pair, tile) is one 128-byte line of codes.  The codes pass through
     // this wave's 4 KiB of the idle staging buffer (16-byte chunk c of row r
     // at r * 128 + 16 (c ^ (r & 7))) so that eight lanes store a row's line
@@ -656,7 +657,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
         const int r = nn * 32 + rl;
-        const int pair = sm.pair[r];
         const float sc = sm.rs[r] * ev.wscale;
         const float wgt = sm.rw[r];
         float amax = 0.f;
@@ -668,15 +668,16 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
             amax = fmaxf(amax, fabsf(acc32[mm][nn][v]));
           }
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const int ex = pair_tile_exp(amax);
-        if (pair >= 0 && h == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
+        const int field = pair_tile_field(amax);
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
+            const int col = 32 * mm + 8 * j + 4 * h;
             *reinterpret_cast<uint2*>(wl + rl * 128 + 16 * ((4 * mm + j) ^ (rl & 7)) + 8 * h) =
-                make_uint2(pair_code2(acc32[mm][nn][4 * j], acc32[mm][nn][4 * j + 1], ex),
-                           pair_code2(acc32[mm][nn][4 * j + 2], acc32[mm][nn][4 * j + 3], ex));
+                make_uint2(pair_code2(acc32[mm][nn][4 * j], acc32[mm][nn][4 * j + 1], field, col),
+                           pair_code2(acc32[mm][nn][4 * j + 2], acc32[mm][nn][4 * j + 3], field, col + 2));
+          }
         store_rows(nn * 32, 32);
       }
     } else {
@@ -685,7 +686,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int r = nb * 16 + l16;
-        const int pair = sm.pair[r];
         const float sc = sm.rs[r] * ev.wscale;
         const float wgt = sm.rw[r];
         float amax = 0.f;
@@ -698,13 +698,14 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const int ex = pair_tile_exp(amax);
-        if (pair >= 0 && g == 0) pair_exps(p)[(size_t)pair * (p.H / 64) + tile_e] = ex;
+        const int field = pair_tile_field(amax);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb) {
+          const int col = 16 * mb + 4 * g;
           *reinterpret_cast<uint2*>(wl + l16 * 128 + 16 * ((2 * mb + g / 2) ^ (l16 & 7)) + 8 * (g % 2)) =
-              make_uint2(pair_code2(acc[mb][nb][0], acc[mb][nb][1], ex),
-                         pair_code2(acc[mb][nb][2], acc[mb][nb][3], ex));
+              make_uint2(pair_code2(acc[mb][nb][0], acc[mb][nb][1], field, col),
+                         pair_code2(acc[mb][nb][2], acc[mb][nb][3], field, col + 2));
+        }
         store_rows(nb * 16, 16);
       }
     }
@@ -765,7 +766,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
             }
             if (r < 0) rem -= c;
           }
-          last_arrival_sum8_xcd(p, sm.tok[r], c0, lane % 8);
+          last_arrival_sum8_xcd(p, sm.tok[r], c0, lane % 8, lane);
         }
       }
     }
