@@ -325,15 +325,15 @@ typedef struct {
   int32_t out_dtype;
   int32_t mode;        /* STORE (dense only) or ACCUMULATE (sorted only) */
   int32_t* counters;   /* ACCUMULATE: moe_stage2_counters(T, H) int32, zero on
-                          entry: [T][H/64] arrival counts, then the work-queue
-                          state of the stage-2 kernels */
+                          entry: [T][H/64] arrival counts (per token and
+                          64-column tile, or per token and group of tiles),
+                          then the work-queue state of the stage-2 kernels */
   int32_t expected_arrivals; /* contributions per token: must equal k_total */
   hipEvent_t addend_ready;   /* waited on (device-side) before stage 2, or NULL */
 } moe_stage_args;
 
 /* Number of int32 counters moe_stage2_accum (ACCUMULATE) needs, all zero on
- * entry: one arrival count per (token, 64-column tile), then 16 words of
- * work-queue state. */
+ * entry: T * (H/64) arrival counts, then 16 words of work-queue state. */
 static inline size_t moe_stage2_counters(int32_t T, int32_t H) { return (size_t)T * (size_t)(H / 64) + 16; }
 
 /* Stage 1 (vLLM PR 65207, "Purpose", commit 2 names the two AITER stages):

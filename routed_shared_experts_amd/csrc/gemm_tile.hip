@@ -141,6 +141,7 @@ struct TileSmem {
   float rw[BM];   // stage 2: pair weight / gate
   float rs[BM];   // row scale (stage 1 A8W8: x scale; stage 2 A8W8: h row scale)
   int item;       // persistent stage 2: the claimed work item / queue
+  uint64_t done[(BM + 63) / 64];  // stage 2, counted per group: rows whose count completed
 };
 
 // LDS offset of 16-byte chunk c (0..7) of row r (0..15) in a staged 16-row
@@ -245,7 +246,7 @@ __device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int t
 // the shared memory).
 template <int FMT, int STAGE, int NB>
 __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB>& sm, int b, const ExpertView& ev,
-                                           int c0, bool wave_ok) {
+                                           int c0, bool wave_ok, int cslot, bool group_count) {
   constexpr int esz = FmtInfo<FMT>::esz;
   constexpr int BM = 16 * NB;                                // sorted rows of a block
   constexpr int CPT = NB / 2;                                // staged 16-byte chunks per thread per K tile
@@ -512,7 +513,8 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 
   // ---- epilogues (per wave, from registers) ----
   // acc[mb][nb][v] = row (mb, 4g + v) of the wave's weight rows x token row nb*16 + l16
-  if (!wave_ok) return;
+  // (counted per group: every wave takes part in the count)
+  if (!wave_ok && !(k32 && STAGE == 2 && p.mode != 0 && group_count)) return;
   // k32: acc32[mm][nn][4 j + v] = weight row 8 j + 4 (l / 32) + v of M block
   // mm x token row nn * 32 + l % 32
   if constexpr (STAGE == 1 && k32) {
@@ -650,7 +652,9 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       }
       wave_lds_sync();  // the next group rewrites the region
     };
-    if constexpr (k32) {
+    if (!wave_ok) {
+      // no columns: this wave only takes part in the count below
+    } else if constexpr (k32) {
       // lanes l and l + 32 hold the tile's 64 columns of token row l % 32 of
       // each 32-row group (columns 32 mm + 8 j + 4 (l / 32) + 0..3)
       const int rl = lane % 32, h = lane / 32;
@@ -707,6 +711,56 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
                          pair_code2(acc[mb][nb][2], acc[mb][nb][3], field, col + 2));
         }
         store_rows(nb * 16, 16);
+      }
+    }
+    if constexpr (k32) {
+      if (group_count) {
+        // One group per queue (H <= 2048): a row counts once for the group,
+        // on the counter (token, cslot), once every wave's stores have
+        // reached the L2 (each wave waits for its acknowledgements, then the
+        // barrier); the first wave counts all rows.  A quarter of the atomics
+        // (measured faster for bf16 there; slower for the fp8 formats).
+        constexpr int ND = (BM + kWave - 1) / kWave;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid < kWave) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int r = d * kWave + lane;
+            int old = -1;
+            if (r < BM && sm.pair[r] >= 0) old = atomicAdd(p.counters + (size_t)sm.tok[r] * (p.H / 64) + cslot, 1);
+            const uint64_t m = __ballot(old == p.expected - 1);
+            if (lane == 0) sm.done[d] = m;
+          }
+        }
+        __syncthreads();
+        if (!wave_ok) return;
+        uint64_t done[ND];
+        int total = 0;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          done[d] = sm.done[d];
+          total += __popcll(done[d]);
+        }
+        // completed rows, compacted 8 at a time: entry i -> lanes 8 (i % 8) .. + 7
+        for (int base = 0; base < total; base += 8) {
+          const int i = base + lane / 8;
+          if (i < total) {
+            int rem = i, r = -1;
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+              const int c = __popcll(done[d]);
+              if (r < 0 && rem < c) {
+                uint64_t m = done[d];
+                for (int k = 0; k < rem; ++k) m &= m - 1;  // drop the lowest rem set bits
+                r = d * kWave + (__ffsll((unsigned long long)m) - 1);
+              }
+              if (r < 0) rem -= c;
+            }
+            last_arrival_sum8_xcd(p, sm.tok[r], c0, lane % 8, lane);
+          }
+        }
+        return;
       }
     }
     // count arrivals once the stores have reached the L2 (their acknowledgement);
@@ -811,13 +865,16 @@ void gemm_tile_kernel(GemmParams p) {
   int c0 = n0 + wv * ((STAGE == 1) ? 32 : 64);
   const bool wave_ok = (STAGE == 1) ? (c0 < ev.width) : true;
   if (!wave_ok) c0 = 0;  // rows past a narrow chunk: read block 0, store nothing
-  tile_block<FMT, STAGE, NB>(p, sm, b, ev, c0, wave_ok);
+  tile_block<FMT, STAGE, NB>(p, sm, b, ev, c0, wave_ok, 0, false);
 }
 
 // Stage 2 ACCUMULATE: persistent workgroups draining the per-XCD queues.
 // Queue x's items are (block b, group j): its waves own the reduction tiles
-// t = x + 8 (4 j + w), w = 0..3 (t < H/64).  Queue state (next item, owner)
-// follows the T * (H/64) arrival counters and is zero on entry.
+// t = x + 8 (4 j + w), w = 0..3 (t < H/64).  A row's arrival is counted on
+// the counter (token, t) of its tile, or (bf16, every queue with one group)
+// once for the group on the counter (token, x) (x * groups + j < H/64 for
+// every non-empty group), among the T * (H/64) counter words.  Queue state
+// (next item, owner) follows the counters and is zero on entry.
 template <int FMT, int NB>
 __global__ __launch_bounds__(kTileThreads)
 __attribute__((amdgpu_waves_per_eu(tile_waves_per_eu<FMT, 2, NB>(), tile_waves_per_eu<FMT, 2, NB>())))
@@ -832,6 +889,7 @@ void gemm_tile_accum_kernel(GemmParams p) {
   int* q_next = p.counters + (size_t)p.T * n64;
   int* q_owner = q_next + kNumXcd;
   const int me = xcc_id();
+  const bool group_count = (n64 + kNumXcd - 1) / kNumXcd <= 4;  // one group per queue
 
   for (int step = 0; step < kNumXcd; ++step) {
     const int q = (me + step) % kNumXcd;
@@ -859,7 +917,7 @@ void gemm_tile_accum_kernel(GemmParams p) {
       const int t = q + kNumXcd * (4 * j + wv);
       const bool wave_ok = t < n64;
       const ExpertView ev = resolve_expert<FMT, 2>(p, e);
-      tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok);
+      tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok, q * groups_q + j, group_count);
       __syncthreads();  // the next item rewrites the row tables
     }
   }
