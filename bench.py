@@ -144,7 +144,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this layer runs on one GPU; --gpus N with N > 1 is not supported "
-                                   "(no collectives or sharding in this build)"}))
+                                   "(the library has no collectives or sharding)"}))
         sys.exit(2)
     import torch
     import workloads
