@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* bad shape, pointer, alignment or parameter */
-  MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not provide */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request the library does not provide */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } moe_status;
