@@ -35,6 +35,14 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
 * gate / expert / layer: pinned -- torch float64 library routines on the
   E = 1 case, dense brute force with unselected weights zeroed, the
   shared-only and scale-folding identities.
+* the fp8 expert chain (MXFP8 and a8w8: bf16 rounding of h, MX-32 or per-row
+  quantisation of h, the row scale times the expert scale): pinned -- an
+  independent torch float64 reference built from the format definitions with
+  torch's float8_e4m3fn and bfloat16 casts, equal h codes and outputs, and
+  planted mistakes in the oracle that the comparison catches.
+* biased sigmoid routing weights: pinned -- closed-form weights
+  sigmoid(l_j) / sum sigmoid(l_sel) * s on a case where the bias changes the
+  selection, with and without groups.
 """
 
 from .codecs import (

@@ -112,17 +112,19 @@ def test_routed_weights_sum_to_scale():
 
 
 def test_a8w8_scales_on_accumulator_equal_dequantise_first():
-    """Applying per-token and per-expert scales to the accumulator equals
-    dequantising first; bit-exact when the scales are powers of two."""
+    """The oracle's expert applies per-token and per-expert scales to the
+    accumulator (AITER PR 6106, Technical Details); with power-of-two scales
+    that equals dequantising the operands first, bit for bit, through the
+    same function."""
     cfg = _small("a8w8", I_s=0)
     inp = _inputs(cfg)
-    inp["x_scale"] = np.exp2(np.round(np.log2(inp["x_scale"]))).astype(np.float32)
-    inp["w13_scale"] = np.exp2(np.round(np.log2(inp["w13_scale"]))).astype(np.float32)
-    xh, sx = L.decode_activations(inp, "a8w8")
-    W13, W2, s13, s2 = L.expert_weights(inp, "a8w8", 0)
-    a_acc = (xh @ W13.T) * sx[:, None] * s13
-    a_deq = (xh * sx[:, None]) @ (W13 * s13).T
-    assert np.array_equal(a_acc, a_deq)
+    sx = np.exp2(np.round(np.log2(inp["x_scale"]))).astype(np.float64)
+    xh, _ = L.decode_activations(inp, "a8w8")
+    W13, W2, _, _ = L.expert_weights(inp, "a8w8", 0)
+    s13, s2 = 2.0 ** -11, 2.0 ** -9
+    o_acc = L.expert_mlp(xh, sx, W13, W2, s13, s2, "a8w8")
+    o_deq = L.expert_mlp(xh * sx[:, None], np.ones(cfg.T), W13 * s13, W2 * s2, 1.0, 1.0, "a8w8")
+    assert np.array_equal(o_acc, o_deq)
 
 
 def test_pseudo_split_of_shared_expert_is_exact_by_linearity():
