@@ -4,7 +4,7 @@ One step = one whole layer forward (routing + gate dot + sort + stage 1 +
 stage 2 with the shared-expert addend) over one batch of seeded synthetic
 inputs already resident in HBM.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload a8w8_large]
                     [--mode auto|pseudo|aux|best] [--graph] [--no-cpu-baseline]
                     [--copy-calibration MIB]
 
@@ -34,19 +34,24 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "a8w8": 5000.
 DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "a8w8": "fp8-e4m3"}
 TIMING_EVERY = 8
 N_EVENTS = 7  # timing events the layer takes (prologue and sort spans, each GEMM kernel's start and end)
-# sources of the GEMM kernels: the stage-1 traffic figure in profiles/ holds
-# only while their hash is the one it was measured with
-KERNEL_SOURCES = ["gemm_wave.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"]
+# sources of the GEMM kernels: a traffic figure in profiles/ holds only while
+# the hash of the sources of the kernel it was measured on is unchanged
+# (16-row one-wave kernels at decode sizes, the tiled kernels otherwise)
+KERNEL_SOURCES = {
+    "wave": ["gemm_wave.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"],
+    "tile": ["gemm_tile.hip", "gemm.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"],
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="a8w8_large")
     ap.add_argument("--mode", default="best", choices=["auto", "pseudo", "aux", "best"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated per step (0 = auto)")
+    ap.add_argument("--block-m", type=int, default=0, help="rows per sorted block (0 = automatic)")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -55,19 +60,20 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(family):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "routed_shared_experts_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per stage-1 launch from the committed profiler summary of this
-    workload (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
-    or None when there is none or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_stage1_traffic.txt")
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of the given GEMM stage from the committed profiler
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by a plain
+    copy's reading), or None when there is none or the kernel sources changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_{stage}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -75,7 +81,8 @@ def measured_traffic(workload):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+    fam = kv.get("kernel_family", "wave")
+    if fam not in KERNEL_SOURCES or kv.get("kernel_sources_sha256") != kernel_sources_sha256(fam):
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
@@ -113,9 +120,22 @@ def algorithmic(cfg, ids, m_pseudo):
     return flops, byt, (s1_flops, s1_bytes), (s2_flops, s2_bytes), active
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, seconds):
-    """The oracle as it stands, on this host, over whole-layer passes of the
-    same workload (decode_bf16: all 32 tokens per pass) until ``seconds``."""
+    """The oracle as it stands, on this host's cores, over passes of the same
+    workload until ``seconds`` have elapsed: every token of the small
+    workloads, a fixed seeded token sample of the large ones (each pass
+    routes all T tokens and runs every expert the sample selects, decoding
+    those experts' weights from the same bytes the GPU reads)."""
     import oracle
     import workloads
     try:
@@ -123,10 +143,10 @@ def cpu_baseline(cfg, inp, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    host = workloads.to_host(inp, lazy_weights=cfg.T * cfg.topk < cfg.E * 4)
-    tokens = np.arange(cfg.T)
-    if cfg.name == "a8w8_large" or cfg.name == "mxfp8" or cfg.name == "prefill_bf16":
-        tokens = np.arange(min(cfg.T, 16))
+    lazy = cfg.T * cfg.topk >= cfg.E * 4
+    host = workloads.to_host(inp, lazy_weights=lazy)
+    n_tok = {"a8w8_large": 4, "mxfp8": 16, "prefill_bf16": 64}.get(cfg.name, cfg.T)
+    tokens = np.sort(np.random.default_rng(20261203).choice(cfg.T, size=n_tok, replace=False))
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -135,7 +155,9 @@ def cpu_baseline(cfg, inp, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    sample = f"{n} oracle passes over {tokens.size} tokens of {cfg.name} ({el:.1f} s)"
+    sample = (f"{n} oracle passes over {tokens.size} of the {cfg.T} tokens of {cfg.name} "
+              f"(seeded sample; routing of all {cfg.T} tokens in every pass), {el:.1f} s "
+              f"on {cpu_model()}")
     return {"value": n * tokens.size / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": sample}
 
@@ -163,7 +185,7 @@ def main():
     modes = ["pseudo", "aux"] if args.mode == "best" else [args.mode]
     results = {}
     for mode in modes:
-        layers = [m.MoeLayer(cfg, inp, shared_mode=mode, packed=pk) for pk in packed_sets]
+        layers = [m.MoeLayer(cfg, inp, shared_mode=mode, packed=pk, block_m=args.block_m) for pk in packed_sets]
         out = layers[0].out
         for L in layers[1:]:
             L.args.out = m._ptr(out)
@@ -264,8 +286,7 @@ def main():
             ach, peak, unit = s_bytes / (s_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
         rec["roofline"] = {"kernel": names[st], "bound": "mfma" if mfma_bound else "hbm",
                            "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
-                           "traffic": (measured_traffic(cfg.name)
-                                       if (best == "pseudo" and st == "stage1" and not mfma_bound) else None),
+                           "traffic": measured_traffic(cfg.name, st) if best == "pseudo" else None,
                            "bytes_per_launch": s_bytes, "flops_per_launch": s_flops,
                            "timed_steps": len(range(0, args.steps, TIMING_EVERY))}
     if args.copy_calibration > 0:

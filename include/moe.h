@@ -28,8 +28,10 @@
  *
  * Conventions for every entry point:
  * - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
- *   aligned, row-major and dense.  The library never allocates, never frees
- *   and keeps no mutable global state; calls are reentrant.
+ *   aligned, row-major and dense.  The library never allocates and never
+ *   frees.  Its only mutable state is one thread-local slot holding the HIP
+ *   error behind the calling thread's last MOE_ERR_HIP (read with
+ *   moe_last_hip_error); calls are otherwise stateless and reentrant.
  * - Every argument is validated on the host before anything is launched; an
  *   invalid call returns an error and launches nothing.  Launch failures
  *   return MOE_ERR_HIP; faults inside kernels surface at the caller's next
@@ -152,7 +154,7 @@ typedef struct {
   moe_weights shared;
   const void* gate_w;  /* [H] in x's dtype (F32/BF16), NULL = ungated (gamma = 1) */
   int32_t shared_mode; /* moe_shared_mode */
-  int32_t block_m;     /* rows per sorted block: 0 = automatic, else 16, 32, 64 or 128 */
+  int32_t block_m;     /* rows per sorted block: 0 = automatic, else 16, 32, 64, 128 or 256 (not F32) */
   /* output */
   void* out;         /* [T][H] */
   int32_t out_dtype; /* F32 or BF16 */
@@ -179,7 +181,12 @@ moe_status moe_validate(const moe_forward_args* a);
  * invalid request).  Depends on shapes, formats, mode and block_m only. */
 size_t moe_workspace_bytes(const moe_forward_args* a);
 
-/* The whole layer.  Launch sequence:
+/* The whole layer: the routed experts' output plus the gated shared expert's,
+ * the shared part either fused into the routed grouped GEMM as always-selected
+ * pseudo-experts (vLLM PR 61503, "Overview": one fused heterogeneous MoE op)
+ * or run on a second stream whose result stage 2 accumulates as its addend
+ * after waiting on a ready event right before stage 2 (vLLM PR 65207,
+ * "Purpose", commit 2).  Launch sequence:
  *   PSEUDO/NONE: prologue (route + gate dot + MX quant of x) -> sort (also
  *                clears the arrival counters) -> stage 1 -> stage 2 (per-pair
  *                rows; the last arrival per (token, column tile) sums them in
@@ -299,7 +306,7 @@ typedef struct {
   const void* x_scale;
   /* sorted problem (from moe_sort_tokens) */
   int32_t dense;
-  int32_t block_m;    /* 16, 32, 64 or 128; dense mode: any of these */
+  int32_t block_m;    /* 16, 32, 64, 128 or 256 (not F32); dense mode: any of these */
   int32_t max_blocks; /* capacity / block_m (sorted) or ceil(T / block_m) (dense) */
   const int32_t* sorted_pair_ids;
   const int32_t* block_expert;

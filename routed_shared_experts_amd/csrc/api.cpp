@@ -82,6 +82,19 @@ struct Plan {
   size_t amax_sh_bytes;
 };
 
+int resolve_mode(const moe_forward_args* a, int fmt);
+
+// 256-row sorted blocks run on the tiled kernels only: both routed stages must
+// fit them (whole 128-column stage-1 workgroups, 32-bit buffer offsets).
+bool big_blocks_fit(const moe_forward_args* a, int fmt) {
+  const int m = resolve_mode(a, fmt) == MOE_SHARED_PSEUDO ? (a->I_s + a->I - 1) / a->I : 0;
+  const size_t esz = fmt == FMT_BF16 ? 2 : 1, hsz = fmt == FMT_A8W8 ? 2 : esz;
+  if (a->I % 128 || (m > 0 && a->I_s % 32)) return false;
+  if ((size_t)a->T * a->H * esz >= 0x7FFFFFFFu) return false;
+  const size_t cap = (size_t)moe_sort_capacity(a->T, a->topk + m, a->E + m, 256);
+  return cap * a->I * hsz < 0x7FFFFFFFu;
+}
+
 moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (!a) return MOE_ERR_INVALID_ARG;
   // T = 0 is an empty batch: valid, and then logits, x, out and the row
@@ -102,7 +115,8 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (a->bias && a->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (a->out_dtype != MOE_F32 && a->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (a->shared_mode < MOE_SHARED_NONE || a->shared_mode > MOE_SHARED_AUTO) return MOE_ERR_INVALID_ARG;
-  if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128)
+  if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128 &&
+      a->block_m != 256)
     return MOE_ERR_INVALID_ARG;
   const int fmt = weights_fmt(a->routed);
   if (fmt < 0) return MOE_ERR_UNSUPPORTED;
@@ -116,6 +130,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
     if ((a->T > 0 && !a->x_row_scale) || ((uintptr_t)a->x_row_scale & 3u)) return MOE_ERR_INVALID_ARG;
   }
   if (fmt == FMT_F32 && a->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (fmt == FMT_F32 && a->block_m == 256) return MOE_ERR_UNSUPPORTED;  // 256-row blocks: tiled kernels only
   const int kt = ktile_elems(fmt);
   if (a->H % kt || a->I % kt || (a->I_s % kt)) return MOE_ERR_INVALID_ARG;
   if (a->H % 64) return MOE_ERR_INVALID_ARG;  // stage-2 column tile
@@ -141,6 +156,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
     return MOE_ERR_INVALID_ARG;
   }
   if ((long long)a->T * (a->topk + 64) >= (1LL << 31) / 2) return MOE_ERR_UNSUPPORTED;
+  if (a->block_m == 256 && !big_blocks_fit(a, fmt)) return MOE_ERR_UNSUPPORTED;
   if (fmt_out) *fmt_out = fmt;
   return MOE_OK;
 }
@@ -175,7 +191,9 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   }
   pl.ss_blocks = pl.self_sort ? pl.E_total * ((a->T + 15) / 16) : 0;
   pl.h_rows = pl.capacity > pl.ss_blocks * 16 ? pl.capacity : pl.ss_blocks * 16;
-  pl.dense_bm = a->block_m ? a->block_m : auto_block_m((double)a->T);
+  // dense (aux-stream) blocks: at most 128 rows, which every kernel provides
+  pl.dense_bm = a->block_m ? (a->block_m < 128 ? a->block_m : 128) : auto_block_m((double)a->T);
+  if (pl.dense_bm > 128) pl.dense_bm = 128;
   pl.dense_blocks = (a->T + pl.dense_bm - 1) / pl.dense_bm;
   const int esz_h = h_elem_bytes(fmt);
   size_t o = 0;
@@ -430,11 +448,13 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   if (!a) return MOE_ERR_INVALID_ARG;
   if (a->T <= 0 || a->H <= 0 || a->E <= 0 || a->I <= 0 || a->I_s < 0 || a->n_pseudo < 0 || a->k_total <= 0)
     return MOE_ERR_INVALID_ARG;
-  if (a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128) return MOE_ERR_INVALID_ARG;
+  if (a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128 && a->block_m != 256)
+    return MOE_ERR_INVALID_ARG;
   if (a->max_blocks <= 0) return MOE_ERR_INVALID_ARG;
   const moe_weights& wf = a->dense ? a->shared : a->routed;
   fmt = weights_fmt(wf);
   if (fmt < 0) return MOE_ERR_UNSUPPORTED;
+  if (fmt == FMT_F32 && a->block_m == 256) return MOE_ERR_UNSUPPORTED;
   if (!weights_ok(wf, fmt)) return MOE_ERR_INVALID_ARG;
   if ((a->n_pseudo > 0 || a->dense) && (a->I_s <= 0 || weights_fmt(a->shared) != fmt || !weights_ok(a->shared, fmt)))
     return MOE_ERR_INVALID_ARG;
@@ -477,6 +497,8 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   g.mode = a->mode;
   g.counters = a->counters;
   g.expected = a->expected_arrivals;
+  // 256-row blocks run on the tiled kernels only
+  if (a->block_m == 256 && !(tile_kernel_fits(g, 1, fmt) && tile_kernel_fits(g, 2, fmt))) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

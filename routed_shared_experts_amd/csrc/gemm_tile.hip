@@ -98,11 +98,12 @@ __device__ __forceinline__ int expert_major(const GemmParams& p, int BM, int n_p
 // loading thread's registers (tid < BM) until the epilogue, so no load of
 // the K loop waits behind them.
 template <int FMT, int STAGE, int BM>
-__device__ __forceinline__ void tile_rows(const GemmParams& p, int b, int tid, int* s_tok, int* s_pair, float& rw,
+__device__ __forceinline__ bool tile_rows(const GemmParams& p, int b, int tid, int* s_tok, int* s_pair, float& rw,
                                           float& rs) {
   const int P = p.T * p.k_total;
   rw = 0.f;
   rs = 1.0f;
+  bool live = false;
   if (tid < BM) {
     const int slot = b * BM + tid;
     int tok = -1, pair = -1;
@@ -119,6 +120,7 @@ __device__ __forceinline__ void tile_rows(const GemmParams& p, int b, int tid, i
     }
     s_tok[tid] = tok;
     s_pair[tid] = pair;
+    live = tok >= 0;
     if (FMT == FMT_A8W8) {
       if (STAGE == 1) {
         rs = tok >= 0 ? static_cast<const float*>(p.x_s)[tok] : 0.f;
@@ -128,6 +130,7 @@ __device__ __forceinline__ void tile_rows(const GemmParams& p, int b, int tid, i
       }
     }
   }
+  return live;
 }
 
 template <int BM>
@@ -165,6 +168,13 @@ __device__ __forceinline__ int lds_chunk_off(int r, int c) {
 constexpr int kPairNonFinite = 255;
 
 __device__ __forceinline__ int16_t* pair_codes(const GemmParams& p) { return reinterpret_cast<int16_t*>(p.pair_out); }
+// Running largest magnitude of a tile that also records non-finite values:
+// a NaN or an infinity makes it +Inf for good (fmaxf alone would drop a NaN),
+// so the tile's field below becomes kPairNonFinite and its sum NaN.
+__device__ __forceinline__ float tile_amax(float amax, float v) {
+  const float m = fabsf(v);
+  return m <= 3.4028234664e38f ? fmaxf(amax, m) : __builtin_inff();
+}
 // The tile's 8-bit exponent field from its largest magnitude.
 __device__ __forceinline__ int pair_tile_field(float amax) {
   if (!(amax <= 3.4028234664e38f)) return kPairNonFinite;  // Inf or NaN
@@ -291,6 +301,8 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   const uint32_t kfrag32 = (uint32_t)(((lane / 32) * 16 + l16) * 16);
   const uint32_t wlane = k32 ? (uint32_t)(((lane % 32) / 16) * ev.nkt * 2048) + kfrag32 : (uint32_t)lane * 16;
 
+  int live = 0;  // live rows of the block (set once its row tables are read)
+
   // ---- staged token rows: chunk q = tid + 256 u is chunk q % 8 of row q / 8;
   // padding rows read past the buffer ----
   __amdgpu_buffer_rsrc_t xrs, xsrs;
@@ -357,7 +369,8 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // token-row register sets in flight: XD = 2 keeps the rows of K tiles
   // kt + 1 and kt + 2 loading while tile kt is multiplied
   constexpr int XD =
-      (((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) || (FMT == FMT_A8W8 && STAGE == 2 && NB == 4))
+      (((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) || (FMT == FMT_A8W8 && STAGE == 2 && NB == 4) ||
+       NB == 16)
           ? 1
           : 2;
   uint4 xr[XD][CPT];
@@ -365,7 +378,8 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   auto load_x = [&](int set, int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) xr[set][u] = tile_load16(xrs, xoff[u], (uint32_t)kt * 128);
+    for (int u = 0; u < CPT; ++u)
+      xr[set][u] = (NB < 16 || 32 * u < live) ? tile_load16(xrs, xoff[u], (uint32_t)kt * 128) : make_uint4(0, 0, 0, 0);
     if constexpr (FMT == FMT_MX) {
       xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);  // tid >= BM: reads 0
     }
@@ -373,7 +387,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   auto store_x = [&](int buf, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
+      if (NB < 16 || 32 * u < live) *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
     }
     if constexpr (FMT == FMT_MX) {
       sm.xsc[buf][tid < BM ? tid : BM] = xsr[set];  // no branch: the other threads write the spare slot
@@ -404,53 +418,61 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // The multiply of a K tile runs at raised wave priority, so a wave with its
   // operands ready keeps the matrix core busy ahead of the SIMD's other wave
   // issuing loads (measured: a8w8 stage 1 -5 %, bf16 and MX unchanged).
+  // k32: four K steps of 16 over the live 32-row token groups; consecutive
+  // MFMAs update different accumulators
+  auto compute_k32 = [&](int buf, const uint4 (&w)[4][2]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) {
+        if (32 * nn >= live) continue;  // wave-uniform: a group of padding rows
+        const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st)]);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+          acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf), acc32[mm][nn],
+              0, 0, 0);
+      }
+  };
   auto compute = [&](int buf, const uint4 (&w)[4][2], const int (&sc)[4]) {
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (k32 && STAGE == 1) {
-      // four K steps of 16; the token fragments of step st + 1 are read
-      // while step st multiplies (LDS latency behind eight MFMAs); the
-      // scheduling groups pin that order (the default schedule reads each
-      // fragment just before its two MFMAs and exposes the LDS latency)
-      __builtin_amdgcn_sched_barrier(0);
-      uint4 bf[2][NN];
-#pragma unroll
-      for (int nn = 0; nn < NN; ++nn)
-        bf[0][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(0)]);
-      __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (st < 3) {
-#pragma unroll
-          for (int nn = 0; nn < NN; ++nn)
-            bf[(st + 1) & 1][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st + 1)]);
-          __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
-        }
+    if constexpr (k32 && STAGE == 1 && NB <= 8) {
+      {
+        // four K steps of 16; the token fragments of step st + 1 are read
+        // while step st multiplies (LDS latency behind eight MFMAs); the
+        // scheduling groups pin that order (the default schedule reads each
+        // fragment just before its two MFMAs and exposes the LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 bf[2][NN];
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn)
+          bf[0][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(0)]);
+        __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-            acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf[st & 1][nn]),
-                acc32[mm][nn], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NN, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    } else if constexpr (k32) {
-      // four K steps of 16; consecutive MFMAs update different accumulators
+        for (int st = 0; st < 4; ++st) {
+          if (st < 3) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+            for (int nn = 0; nn < NN; ++nn)
+              bf[(st + 1) & 1][nn] = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st + 1)]);
+            __builtin_amdgcn_sched_group_barrier(0x100, NN, 0);
+          }
 #pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-          const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st)]);
+          for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-            acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf), acc32[mm][nn],
-                0, 0, 0);
+            for (int mm = 0; mm < 2; ++mm)
+              acc32[mm][nn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, w[2 * mm + st / 2][st % 2]), __builtin_bit_cast(bf16x8, bf[st & 1][nn]),
+                  acc32[mm][nn], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NN, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (k32) {
+      compute_k32(buf, w);
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
+        if (NB == 16 && 16 * nb >= live) continue;  // wave-uniform: a group of padding rows
         const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo0]);
         const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo1]);
         const int sb = (FMT == FMT_MX) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
@@ -475,9 +497,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   load_w(wA, sA, 0);
   load_w(wB, sB, 1);
   float rw_row, rs_row;
-  tile_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, rw_row, rs_row);
-  __syncthreads();
-  if (sm.tok[0] < 0) return;  // a block part holding only padding rows (padding sits at the end)
+  // live rows: a block's real rows come first and its padding last, so the
+  // live rows are rows 0 .. live-1; the loads and multiplies of 32-row (16-row)
+  // groups past them are skipped (wave-uniform branches)
+  live = __syncthreads_count(tile_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, rw_row, rs_row));
+  if (live == 0) return;  // a block part holding only padding rows
   row_offsets();
   if constexpr (XD == 2) {
     load_x(0, 0);
@@ -669,7 +693,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             acc32[mm][nn][v] = wgt * (acc32[mm][nn][v] * sc);
-            amax = fmaxf(amax, fabsf(acc32[mm][nn][v]));
+            amax = tile_amax(amax, acc32[mm][nn][v]);
           }
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
         const int field = pair_tile_field(amax);
@@ -698,7 +722,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             acc[mb][nb][v] = wgt * (acc[mb][nb][v] * sc);
-            amax = fmaxf(amax, fabsf(acc[mb][nb][v]));
+            amax = tile_amax(amax, acc[mb][nb][v]);
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
@@ -833,6 +857,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 // for the 64-row a8w8 stage-2 items).
 template <int FMT, int STAGE, int NB>
 constexpr int tile_waves_per_eu() {
+  if (NB == 16) return 1;  // 256-row blocks: 256 accumulator registers per lane
   if (FMT == FMT_A8W8 && STAGE == 2 && NB == 4) return 3;  // with one token-row set in flight (a8w8 stage 2 -2 %)
   return (FMT == FMT_BF16 || NB <= 4 || (FMT == FMT_A8W8 && STAGE == 1)) ? 2 : 1;
 }
@@ -929,7 +954,7 @@ void gemm_tile_accum_kernel(GemmParams p) {
 // addressed with 32-bit buffer offsets.
 bool tile_kernel_fits(const GemmParams& p, int stage, int fmt) {
   if (fmt == FMT_F32) return false;
-  if (p.block_m != 32 && p.block_m != 64 && p.block_m != 128) return false;
+  if (p.block_m != 32 && p.block_m != 64 && p.block_m != 128 && p.block_m != 256) return false;
   const size_t esz = fmt == FMT_BF16 ? 2 : 1;
   const size_t hsz = fmt == FMT_A8W8 ? 2 : esz;
   if (stage == 1) {
@@ -967,6 +992,7 @@ static hipError_t launch_tile_fs(const GemmParams& p, hipStream_t s) {
     case 32: return launch_tile_nb<FMT, STAGE, 2>(p, s);
     case 64: return launch_tile_nb<FMT, STAGE, 4>(p, s);
     case 128: return launch_tile_nb<FMT, STAGE, 8>(p, s);
+    case 256: return launch_tile_nb<FMT, STAGE, 16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

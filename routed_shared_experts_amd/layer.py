@@ -40,9 +40,11 @@ def pack_weights(cfg, inp, stream=None):
     return out
 
 
-def forward_args(cfg, inp, out, shared_mode="auto", block_m=0):
-    """Fill a MoeForwardArgs from a workload config and its input tensors."""
+def forward_args(cfg, inp, out, shared_mode="auto", block_m=0, out_dtype=None):
+    """Fill a MoeForwardArgs from a workload config and its input tensors
+    (out_dtype: MOE_F32 or MOE_BF16; None = the format's own output type)."""
     xdt, _, _, odt = FORMATS[cfg.fmt]
+    odt = odt if out_dtype is None else out_dtype
     a = MoeForwardArgs()
     a.T, a.H, a.E, a.I, a.I_s, a.topk = cfg.T, cfg.H, cfg.E, cfg.I, cfg.I_s, cfg.topk
     a.score = MOE_SCORE_SOFTMAX if cfg.score == "softmax" else MOE_SCORE_SIGMOID
@@ -73,16 +75,18 @@ class MoeLayer:
     aux-stream mode, a second stream and two events.
     """
 
-    def __init__(self, cfg, inp, shared_mode="auto", block_m=0, out=None, packed=None):
+    def __init__(self, cfg, inp, shared_mode="auto", block_m=0, out=None, packed=None, out_dtype=None):
         """inp: the workload's tensors with row-major weights; packed: their
-        tiled copies from pack_weights (made here when None)."""
+        tiled copies from pack_weights (made here when None); out_dtype:
+        MOE_F32 or MOE_BF16 (None: the format's own output type)."""
         packed = pack_weights(cfg, inp) if packed is None else packed
         inp = dict(inp, **packed)
         self.cfg, self.inp = cfg, inp
         dev = inp["x"].device
-        odt = torch.float32 if FORMATS[cfg.fmt][3] == MOE_F32 else torch.bfloat16
+        odt_c = FORMATS[cfg.fmt][3] if out_dtype is None else out_dtype
+        odt = torch.float32 if odt_c == MOE_F32 else torch.bfloat16
         self.out = out if out is not None else torch.empty((cfg.T, cfg.H), dtype=odt, device=dev)
-        self.args = forward_args(cfg, inp, self.out, shared_mode, block_m)
+        self.args = forward_args(cfg, inp, self.out, shared_mode, block_m, odt_c)
         st = moe_validate(self.args)
         if st != MOE_OK:
             raise MoeError(f"moe_validate: {moe_status_str(st)}")

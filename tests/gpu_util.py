@@ -23,9 +23,9 @@ def inputs(cfg, device):
     return _cache[key]
 
 
-def run_forward(cfg, inp, mode="auto", block_m=0):
+def run_forward(cfg, inp, mode="auto", block_m=0, out_dtype=None):
     import routed_shared_experts_amd as m
-    layer = m.MoeLayer(cfg, inp, shared_mode=mode, block_m=block_m)
+    layer = m.MoeLayer(cfg, inp, shared_mode=mode, block_m=block_m, out_dtype=out_dtype)
     out = layer.forward()
     torch.cuda.synchronize()
     return out, layer
@@ -41,12 +41,14 @@ def compare(cfg, out, inp, tokens=None, lazy=False):
         got = got[np.asarray(tokens)]
     rms = np.sqrt((y ** 2).mean())
     err = np.abs(got - y).max()
-    # rounding floor of a single final rounding to the output type
-    if cfg.fmt == "f32":
-        floor = np.abs(y).max() * 2.0 ** -24
-    else:
-        floor = 2.0 ** -9 * 2.0 ** np.floor(np.log2(np.abs(y).max()))
-    return err / rms, floor / rms, r
+    return err / rms, rounding_floor(y, out.dtype) / rms, r
+
+
+def rounding_floor(y, dtype):
+    """Largest error one correct rounding of y to the output type can make:
+    half an ulp in the binade of max |y| (bf16: 8 significant bits)."""
+    top = 2.0 ** np.floor(np.log2(np.abs(y).max()))
+    return top * (2.0 ** -24 if dtype == torch.float32 else 2.0 ** -8)
 
 
 def assert_close(cfg, out, inp, tokens=None, lazy=False):

@@ -1,0 +1,344 @@
+"""Full-size parity that reaches every sorted block, determinism, the
+stage-1 intermediate against the oracle, and non-finite values in the tiled
+stage-2 reduction.
+
+The workloads are compared with the oracle on token sets chosen from the
+routing (bit-exact against the oracle's, tested elsewhere): for every sorted
+block of every expert -- and every 64-row half of a 128-row block, the unit
+of the stage-2 work queues -- the tokens of its first and last real rows are
+compared, plus a seeded random sample.  Each workload runs in both shared
+modes against one oracle evaluation."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, inputs, run_forward, rounding_floor
+
+pytestmark = pytest.mark.gpu
+
+LC = workloads.LayerConfig
+
+
+def _auto_block_m(rows_per_expert):
+    need = 1.5 * rows_per_expert
+    for bm in (16, 32, 64):
+        if need <= bm:
+            return bm
+    return 128
+
+
+def covering_tokens(cfg, ids, n_random, seed):
+    """Tokens whose rows are the first and the last real row of every 64-row
+    part of every sorted block, in both shared modes, plus n_random others."""
+    T, k = ids.shape
+    toks = set()
+    m = cfg.n_pseudo
+    for k_total, n_exp, full in ((k, cfg.E, ids),
+                                 (k + m, cfg.E + m,
+                                  np.concatenate([ids, np.tile(np.arange(cfg.E, cfg.E + m), (T, 1))], 1))):
+        bm = _auto_block_m(T * k_total / n_exp)
+        srt = oracle.sort_tokens(full, n_exp, bm)["sorted_pair_ids"]
+        P = T * k_total
+        part = min(bm, 64)
+        for b0 in range(0, srt.size, part):
+            real = srt[b0:b0 + part]
+            real = real[real < P]
+            if real.size:
+                toks.add(int(real[0]) // k_total)
+                toks.add(int(real[-1]) // k_total)
+    rng = np.random.default_rng(seed)
+    toks |= set(int(t) for t in rng.choice(T, size=min(n_random, T), replace=False))
+    toks |= {0, T - 1}
+    return np.array(sorted(toks))
+
+
+def _route_ids(cfg, inp):
+    host = workloads.to_host({"logits": inp["logits"], "bias": inp.get("bias")})
+    ids, _ = oracle.route(host["logits"], topk=cfg.topk, score=cfg.score, bias=host["bias"],
+                          n_group=cfg.n_group, topk_group=cfg.topk_group,
+                          group_score_topk=cfg.group_score_topk, renormalize=cfg.renormalize,
+                          routed_scaling_factor=cfg.routed_scaling_factor)
+    return ids
+
+
+def _check_both_modes(cfg, inp, tokens, lazy):
+    """Both shared modes against one oracle evaluation.  The layer's
+    arithmetic is held to the format's bound with an fp32 output (the same
+    kernels; only the final store differs), the bf16 output must be exactly
+    the round-to-nearest-even of that fp32 output (the one final rounding),
+    and its error against the unrounded reference is then at most the bound
+    plus half a bf16 ulp at the largest output."""
+    import routed_shared_experts_amd as m
+    outs = {}
+    for mode in ("pseudo", "aux"):
+        o32, _ = run_forward(cfg, inp, mode, out_dtype=m.MOE_F32)
+        o32 = o32.clone()
+        o16, _ = run_forward(cfg, inp, mode)
+        assert torch.equal(o16, o32.to(torch.bfloat16)), f"{cfg.name}/{mode}: bf16 output is not RNE(fp32 output)"
+        outs[mode] = (o32.cpu().numpy().astype(np.float64)[tokens], o16.float().cpu().numpy().astype(np.float64)[tokens])
+        del o32, o16
+    host = workloads.to_host(inp, lazy_weights=lazy)
+    y = oracle.moe_layer(host, cfg, tokens=tokens)["y"]
+    rms = np.sqrt((y ** 2).mean())
+    floor = rounding_floor(y, torch.bfloat16) / rms
+    for mode, (g32, g16) in outs.items():
+        rel = np.abs(g32 - y).max() / rms
+        rel16 = np.abs(g16 - y).max() / rms
+        print(f"{cfg.name}/{mode}: {tokens.size} tokens, max|err|/rms={rel:.3e} with fp32 output "
+              f"(bound {TOL[cfg.fmt]}); bf16 output {rel16:.3e} (bound + rounding floor {TOL[cfg.fmt] + floor:.3e})",
+              flush=True)
+        assert rel <= TOL[cfg.fmt], f"{cfg.name}/{mode}: {rel:.3e}"
+        assert rel16 <= TOL[cfg.fmt] + floor, f"{cfg.name}/{mode}: bf16 {rel16:.3e}"
+
+
+def test_prefill_bf16_every_token(gpu):
+    cfg = workloads.CONFIGS["prefill_bf16"]
+    inp = inputs(cfg, gpu)
+    _check_both_modes(cfg, inp, np.arange(cfg.T), lazy=False)
+
+
+def test_mxfp8_every_token(gpu):
+    cfg = workloads.CONFIGS["mxfp8"]
+    inp = inputs(cfg, gpu)
+    _check_both_modes(cfg, inp, np.arange(cfg.T), lazy=True)
+
+
+def test_a8w8_large_every_block(gpu):
+    cfg = workloads.CONFIGS["a8w8_large"]
+    inp = inputs(cfg, gpu)
+    ids = _route_ids(cfg, inp)
+    tokens = covering_tokens(cfg, ids, 1024, 3)
+    print(f"a8w8_large: {tokens.size} tokens cover every 64-row part of every sorted block", flush=True)
+    assert tokens.size >= 1024
+    _check_both_modes(cfg, inp, tokens, lazy=True)
+
+
+@pytest.mark.parametrize("block_m", [16, 64, 128, 256])
+@pytest.mark.parametrize("mode", ["pseudo", "aux"])
+def test_repeated_forwards_are_bitwise_identical(gpu, block_m, mode):
+    """The stage-2 reduction sums each token's contributions in slot order
+    whichever workgroup finishes last, so repeated forwards give the same
+    bits (one-wave kernels at 16 rows, tiled kernels at 64 and 128)."""
+    cfg = LC("det", T=300, H=512, E=16, I=256, I_s=256, topk=4, fmt="bf16", logits="zipf", zipf_s=1.1)
+    inp = inputs(cfg, gpu)
+    a, layer = run_forward(cfg, inp, mode, block_m=block_m)
+    a = a.clone()
+    for _ in range(4):
+        b = layer.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+# ---- stage-1 intermediate h against the oracle's ---------------------------
+
+def _stage1_h(cfg, inp, block_m, dev):
+    """Sort + stage 1 through the C ABI (no shared expert).  Returns the
+    sorted pair ids and the stage-1 output as stored: bf16 bits (bf16, a8w8:
+    the bf16 values before the per-row quantisation of stage 2, plus the row
+    maxima) or MX codes and scale bytes (mxfp8)."""
+    import routed_shared_experts_amd as m
+    from routed_shared_experts_amd import _ptr
+    from routed_shared_experts_amd.layer import weights_struct, pack_weights
+
+    W = dict(inp, **pack_weights(cfg.replace(I_s=0), inp))
+    T, H, E, I, k = cfg.T, cfg.H, cfg.E, cfg.I, cfg.topk
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    m.moe_route(W["logits"], ids, w, topk=k, bias=W.get("bias"), n_group=cfg.n_group, topk_group=cfg.topk_group,
+                group_score_topk=cfg.group_score_topk,
+                score=m.MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else m.MOE_SCORE_SOFTMAX,
+                renormalize=cfg.renormalize, routed_scaling_factor=cfg.routed_scaling_factor)
+    if cfg.fmt == "mxfp8":
+        x = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        x_scale = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        m.moe_quant_mx(W["x"], x, x_scale)
+    else:
+        x, x_scale = W["x"], W.get("x_scale")
+    cap = m.moe_sort_capacity(T, k, E, block_m)
+    srt = torch.empty((cap,), dtype=torch.int32, device=dev)
+    bexp = torch.empty((cap // block_m,), dtype=torch.int32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    nblk = torch.empty((4,), dtype=torch.int32, device=dev)
+    m.moe_sort_tokens(ids, E, block_m, cap, srt, bexp, counts, offs, nblk)
+    if cfg.fmt == "mxfp8":
+        h = torch.empty((cap, I), dtype=torch.uint8, device=dev)
+        hs = torch.empty((cap, I // 32), dtype=torch.uint8, device=dev)
+    else:
+        h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+        hs = torch.zeros((cap,), dtype=torch.float32, device=dev) if cfg.fmt == "a8w8" else None
+    a = m.MoeStageArgs()
+    a.T, a.H, a.E, a.I, a.I_s, a.n_pseudo, a.k_total = T, H, E, I, 0, 0, k
+    a.routed = weights_struct(W["w13"], W["w2"], W.get("w13_scale"), W.get("w2_scale"), cfg.fmt)
+    a.x, a.x_scale = _ptr(x), _ptr(x_scale)
+    a.dense, a.block_m, a.max_blocks = 0, block_m, cap // block_m
+    a.sorted_pair_ids, a.block_expert, a.num_blocks = _ptr(srt), _ptr(bexp), _ptr(nblk)
+    a.h, a.h_scale = _ptr(h), _ptr(hs)
+    m.moe_stage1(a)
+    torch.cuda.synchronize()
+    if cfg.fmt == "mxfp8":
+        return srt.cpu().numpy(), h.cpu().numpy(), hs.cpu().numpy()
+    bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    return srt.cpu().numpy(), bits, (hs.cpu().numpy() if hs is not None else None)
+
+
+def _adjacent(a, b, sign_bit, mag_mask):
+    """Codes one step apart (or equal) in a sign-magnitude format whose
+    magnitudes are ordered like the codes (bf16 and e4m3fn both are)."""
+    a, b = a.astype(np.int64), b.astype(np.int64)
+    sa, sb = a & sign_bit, b & sign_bit
+    ma, mb = a & mag_mask, b & mag_mask
+    return np.where(sa == sb, np.abs(ma - mb) <= 1, (ma + mb) <= 1)
+
+
+STAGE1_CASES = {
+    "bf16": LC("s1_bf16", T=200, H=512, E=8, I=256, I_s=0, topk=2, fmt="bf16", logits="zipf", zipf_s=1.1,
+               gated=False),
+    "mxfp8": LC("s1_mxfp8", T=120, H=512, E=16, I=256, I_s=0, topk=4, score="sigmoid", n_group=4, topk_group=2,
+                fmt="mxfp8", gated=False, bias_std=0.1),
+    "a8w8": LC("s1_a8w8", T=120, H=512, E=16, I=256, I_s=0, topk=4, score="sigmoid", n_group=4, topk_group=2,
+               fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+}
+
+
+@pytest.mark.parametrize("block_m", [16, 64, 128, 256])
+@pytest.mark.parametrize("name", list(STAGE1_CASES))
+def test_stage1_intermediate_matches_oracle(gpu, name, block_m):
+    """Every h row of stage 1 against the oracle's intermediate: the bf16
+    rounding of SiLU(gate) * up (bf16 and a8w8; a8w8 also the row maxima
+    stage 2 derives its row scales from) or its MX-32 codes and block scales
+    (mxfp8).  The GPU accumulates in fp32 and the oracle in fp64, so a value
+    near a rounding boundary can land on the neighbouring code; such flips
+    must be rare and one code apart, or, for values far below their row's
+    (MX block's) largest, within 2^-12 of that largest magnitude -- the size
+    of the fp32 accumulation error there.  An MX block whose largest value flips
+    across a power of two changes its scale by one, which requantises the
+    block: those blocks are counted, not compared code by code."""
+    cfg = STAGE1_CASES[name]
+    inp = inputs(cfg, gpu)
+    srt, got, got_s = _stage1_h(cfg, inp, block_m, gpu)
+    host = workloads.to_host(inp)
+    ids, _ = oracle.route(host["logits"], topk=cfg.topk, score=cfg.score, bias=host.get("bias"),
+                          n_group=cfg.n_group, topk_group=cfg.topk_group, group_score_topk=cfg.group_score_topk)
+    P = cfg.T * cfg.topk
+    flat = ids.reshape(-1)
+    n_val = n_flip = n_blk = n_blk_flip = 0
+    for e in range(cfg.E):
+        slots = np.nonzero((srt < P) & np.isin(srt, np.nonzero(flat == e)[0]))[0]
+        if slots.size == 0:
+            continue
+        inter = oracle.stage1_reference(host, cfg, e, srt[slots] // cfg.topk)
+        ref_bits = oracle.round_to_bf16_bits(inter["h"])
+        if cfg.fmt in ("bf16", "a8w8"):
+            g = got[slots]
+            diff = g != ref_bits
+            gv, rv = oracle.bf16_bits_to_f64(g), oracle.bf16_bits_to_f64(ref_bits)
+            row_max = np.abs(rv).max(axis=1, keepdims=True)
+            ok = _adjacent(g, ref_bits, 0x8000, 0x7FFF) | (np.abs(gv - rv) <= 2.0 ** -12 * row_max)
+            assert ok[diff].all(), name
+            n_val += diff.size
+            n_flip += int(diff.sum())
+            if cfg.fmt == "a8w8":
+                amax = np.abs(oracle.bf16_bits_to_f64(g)).max(axis=1).astype(np.float32)
+                assert np.array_equal(got_s[slots], amax), "row maxima differ from the rows' own values"
+        else:
+            rs, rq = oracle.mx_quantize(oracle.bf16_bits_to_f64(ref_bits).astype(np.float32))
+            gs, gq = got_s[slots], got[slots]
+            same = gs == rs
+            assert (np.abs(gs.astype(int) - rs.astype(int)) <= 1).all(), "an MX block scale moved by more than one"
+            n_blk += same.size
+            n_blk_flip += int((~same).sum())
+            cmp = np.repeat(same, 32, axis=1)
+            diff = (gq != rq) & cmp
+            # one code apart, or (small values) within 2^-12 of the block's
+            # largest magnitude, where the fp32 accumulation error lives
+            gv, rv = oracle.mx_dequantize(gs, gq), oracle.mx_dequantize(rs, rq)
+            blk_max = np.repeat(np.abs(rv).reshape(rv.shape[0], -1, 32).max(axis=2), 32, axis=1)
+            ok = _adjacent(gq, rq, 0x80, 0x7F) | (np.abs(gv - rv) <= 2.0 ** -12 * blk_max)
+            assert ok[diff].all(), name
+            n_val += int(cmp.sum())
+            n_flip += int(diff.sum())
+    rate = n_flip / max(n_val, 1)
+    msg = f"stage 1 {name}/bm{block_m}: {n_flip} of {n_val} values one code from the oracle's (rate {rate:.2e})"
+    if cfg.fmt == "mxfp8":
+        msg += f"; {n_blk_flip} of {n_blk} MX blocks with a scale one step off"
+        assert n_blk_flip <= 0.01 * n_blk
+    print(msg)
+    # the fp8 formats' 16x16x128 MFMA sums its 128 products to about 15 bits
+    # relative to the sum of their magnitudes (measured on MI355X: at most
+    # 2^-15.2, mean 1.3e-6), far coarser than fp32 addition; a8w8's unit-scale
+    # codes put many h values that close to a bf16 rounding boundary
+    assert rate <= {"bf16": 1e-3, "mxfp8": 1e-2, "a8w8": 5e-2}[cfg.fmt]
+
+
+# ---- non-finite values in the stage-2 reduction ------------------------------
+
+def _stage2_with_bad_h(cfg, inp, block_m, dev, bad):
+    """Route, sort, stage 1; then plant NaN / Inf into h at the given
+    (sorted rank of a live row, column) places; then ACCUMULATE stage 2.
+    Returns out (float64) and the tokens hit."""
+    import routed_shared_experts_amd as m
+    from routed_shared_experts_amd import _ptr
+    from routed_shared_experts_amd.layer import weights_struct, pack_weights
+
+    W = dict(inp, **pack_weights(cfg, inp))
+    T, H, E, I, k = cfg.T, cfg.H, cfg.E, cfg.I, cfg.topk
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    m.moe_route(W["logits"], ids, w, topk=k)
+    cap = m.moe_sort_capacity(T, k, E, block_m)
+    srt = torch.empty((cap,), dtype=torch.int32, device=dev)
+    bexp = torch.empty((cap // block_m,), dtype=torch.int32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    nblk = torch.empty((4,), dtype=torch.int32, device=dev)
+    m.moe_sort_tokens(ids, E, block_m, cap, srt, bexp, counts, offs, nblk)
+    h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+    a = m.MoeStageArgs()
+    a.T, a.H, a.E, a.I, a.I_s, a.n_pseudo, a.k_total = T, H, E, I, 0, 0, k
+    a.routed = weights_struct(W["w13"], W["w2"], None, None, "bf16")
+    a.x = _ptr(W["x"])
+    a.dense, a.block_m, a.max_blocks = 0, block_m, cap // block_m
+    a.sorted_pair_ids, a.block_expert, a.num_blocks = _ptr(srt), _ptr(bexp), _ptr(nblk)
+    a.h = _ptr(h)
+    m.moe_stage1(a)
+    torch.cuda.synchronize()
+    s = srt.cpu().numpy()
+    live = np.nonzero(s < T * k)[0]
+    hit = []
+    for rank, col, val in bad:
+        slot = int(live[rank])
+        h[slot, col] = val
+        hit.append(int(s[slot]) // k)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    counters = torch.zeros((T * (H // 64) + 16,), dtype=torch.int32, device=dev)
+    pair_out = torch.empty((T * k * H,), dtype=torch.float32, device=dev)
+    a.pair_w, a.pair_out, a.out, a.out_dtype = _ptr(w), _ptr(pair_out), _ptr(out), m.MOE_BF16
+    a.mode, a.counters, a.expected_arrivals = m.MOE_STAGE2_ACCUMULATE, _ptr(counters), k
+    m.moe_stage2_accum(a)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), sorted(set(hit))
+
+
+def test_nonfinite_h_reaches_exactly_its_tokens(gpu):
+    """One NaN and one Inf planted in h: the tokens of those rows come out
+    non-finite in every column (each output column reads the whole h row),
+    every other token stays finite and equal to the same layer without the
+    planted values; the tiled kernels (64-row blocks, 16-bit pair rows) and
+    the one-wave kernels (16-row blocks, fp32 pair rows) agree on which."""
+    cfg = LC("nonfinite", T=96, H=512, E=8, I=128, I_s=0, topk=2, fmt="bf16", logits="iid", gated=False)
+    inp = inputs(cfg, gpu)
+    res = {}
+    for bm in (16, 64):
+        clean, _ = _stage2_with_bad_h(cfg, inp, bm, gpu, [])
+        dirty, hit = _stage2_with_bad_h(cfg, inp, bm, gpu, [(3, 5, float("nan")), (40, 77, float("inf"))])
+        bad_rows = np.nonzero(~np.isfinite(dirty).all(axis=1))[0]
+        assert bad_rows.tolist() == hit, (bm, bad_rows, hit)
+        assert (~np.isfinite(dirty[hit])).all(), bm
+        ok = np.setdiff1d(np.arange(cfg.T), hit)
+        assert np.array_equal(dirty[ok], clean[ok]), bm
+        res[bm] = (np.isfinite(dirty), clean)
+    assert np.array_equal(res[16][0], res[64][0])

@@ -24,18 +24,24 @@ SMALL = {
                       topk_group=2, routed_scaling_factor=2.5, fmt="mxfp8", gated=False, bias_std=0.1),
     "small_a8w8": LC("small_a8w8", T=90, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                      topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    # H = 2112: 33 stage-2 column tiles, several tile groups per XCD queue, so
+    # the bf16 reduction counts arrivals per (token, tile) instead of per group
+    "wide_bf16": LC("wide_bf16", T=150, H=2112, E=8, I=128, I_s=128, topk=2, fmt="bf16", logits="zipf",
+                    zipf_s=1.1),
 }
 
 
-@pytest.mark.parametrize("block_m", [0, 16, 32, 128])
+@pytest.mark.parametrize("block_m", [0, 16, 32, 128, 256])
 @pytest.mark.parametrize("mode", ["pseudo", "aux"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layers_all_outputs(gpu, name, mode, block_m):
-    """block_m = 16 takes the one-wave register-streamed GEMM kernels; 32-128
+    """block_m = 16 takes the one-wave register-streamed GEMM kernels; 32-256
     take the tiled kernels (weights in registers, token rows through LDS) for
-    bf16 / MX / a8w8 and the LDS-staged fallback for f32; 0 is the automatic
-    choice."""
+    bf16 / MX / a8w8 and the LDS-staged fallback for f32 (up to 128); 0 is the
+    automatic choice."""
     cfg = SMALL[name]
+    if cfg.fmt == "f32" and block_m == 256:
+        pytest.skip("256-row blocks are provided by the tiled kernels only (not f32)")
     if mode == "pseudo" and cfg.fmt == "a8w8" and cfg.I_s > cfg.I:
         pytest.skip("per-row fp8 intermediate needs a single pseudo chunk")
     inp = inputs(cfg, gpu)
@@ -44,7 +50,7 @@ def test_small_layers_all_outputs(gpu, name, mode, block_m):
     print(f"{name}/{mode}/bm{block_m}: max|err|/rms={rel:.3e} floor={floor:.3e}")
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
 def test_block_m_variants(gpu, block_m):
     cfg = SMALL["small_bf16"]
     inp = inputs(cfg, gpu)
