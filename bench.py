@@ -39,7 +39,8 @@ N_EVENTS = 7  # timing events the layer takes (prologue and sort spans, each GEM
 # (16-row one-wave kernels at decode sizes, the tiled kernels otherwise)
 KERNEL_SOURCES = {
     "wave": ["gemm_wave.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"],
-    "tile": ["gemm_tile.hip", "gemm.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp"],
+    "tile": ["gemm_tile.hip", "gemm_lds.hip", "tile_common.hpp", "gemm.hip", "gemm_common.hpp", "common.hpp",
+             "kernels.hpp"],
 }
 
 

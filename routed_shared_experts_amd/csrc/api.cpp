@@ -84,8 +84,9 @@ struct Plan {
 
 int resolve_mode(const moe_forward_args* a, int fmt);
 
-// 256-row sorted blocks run on the tiled kernels only: both routed stages must
-// fit them (whole 128-column stage-1 workgroups, 32-bit buffer offsets).
+// 256-row sorted blocks run on the LDS-staged kernels only: both routed
+// stages must fit them (whole 128-column stage-1 workgroups, 32-column pseudo
+// chunks, 32-bit buffer offsets).
 bool big_blocks_fit(const moe_forward_args* a, int fmt) {
   const int m = resolve_mode(a, fmt) == MOE_SHARED_PSEUDO ? (a->I_s + a->I - 1) / a->I : 0;
   const size_t esz = fmt == FMT_BF16 ? 2 : 1, hsz = fmt == FMT_A8W8 ? 2 : esz;
@@ -497,8 +498,13 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   g.mode = a->mode;
   g.counters = a->counters;
   g.expected = a->expected_arrivals;
-  // 256-row blocks run on the tiled kernels only
-  if (a->block_m == 256 && !(tile_kernel_fits(g, 1, fmt) && tile_kernel_fits(g, 2, fmt))) return MOE_ERR_UNSUPPORTED;
+  // 256-row blocks run on the LDS-staged kernels only (sorted problem, the
+  // ACCUMULATE stage 2)
+  if (a->block_m == 256) {
+    GemmParams g2 = g;
+    g2.mode = MOE_STAGE2_ACCUMULATE;
+    if (!lds_kernel_fits(g, 1, fmt) || !lds_kernel_fits(g2, 2, fmt)) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 

@@ -382,6 +382,8 @@ hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStrea
   // one wave per 32 (stage 1) or 64 (stage 2) columns of a block
   if (p.block_m == 16 && wave_kernel_fits(p, stage, fmt)) return launch_gemm_wave(p, stage, fmt, s);
   if (p.self_sort) return hipErrorInvalidValue;  // only the one-wave kernels scan the ids
+  // 256-row sorted blocks: both operands through LDS, eight waves
+  if (p.block_m == 256) return lds_kernel_fits(p, stage, fmt) ? launch_gemm_lds(p, stage, fmt, s) : hipErrorInvalidValue;
   // 32-128-row blocks: weights streamed into registers, token rows through LDS.
   // The stage-2 reduction runs 128-row sorted blocks as two 64-row halves
   // (more workgroups per CU; measured faster on MI355X).

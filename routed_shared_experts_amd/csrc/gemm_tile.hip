@@ -45,53 +45,11 @@
 // the counters (device-scope atomics).  A queue is claimed by the first XCD
 // that touches it; an XCD whose own workgroups never arrive has its queue
 // claimed and drained by another, which keeps the property.
-#include "gemm_common.hpp"
+#include "tile_common.hpp"
 
 namespace moe {
 
 constexpr int kTileThreads = 256;
-constexpr int kNumXcd = 8;
-constexpr uint32_t kTileOutOfRange = 0x80000000u;  // buffer offset past every range: reads zero
-
-// Bijection of [0, active) that gives each XCD (blockIdx % 8) a contiguous
-// range of logical tile indices.
-__device__ __forceinline__ int xcd_remap(int bid, int active) {
-  const int q = active / kNumXcd, r = active % kNumXcd;
-  const int x = bid % kNumXcd, i = bid / kNumXcd;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-}
-
-// The XCD this wave runs on (HW_REG_XCC_ID, bits 2:0).
-__device__ __forceinline__ int xcc_id() {
-  return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & (kNumXcd - 1);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
-  // raw (untyped) buffer, dword 3 = 0x00020000 on gfx9-family parts
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
-// Expert-major order of a launch's work: the items of expert e (its blocks x
-// n_per column tiles, a contiguous range in block-major order) are taken
-// column tile by column tile, the blocks of one column tile side by side, so
-// the concurrent workgroups of an expert share each weight tile through L2
-// instead of streaming the expert's weights once per block.  In: the item
-// index `it` of block-major order; out: block b and column tile c; returns
-// the expert.
-__device__ __forceinline__ int split_of(const GemmParams& p) { return p.bsplit > 1 ? p.bsplit : 1; }
-
-__device__ __forceinline__ int expert_major(const GemmParams& p, int BM, int n_per, int it, int& b, int& c) {
-  const int e = p.block_expert[it / n_per / split_of(p)];
-  const int bs = p.offsets[e] / BM, nb = (p.offsets[e + 1] - p.offsets[e]) / BM;
-  const int local = it - bs * n_per;
-  c = local / nb;
-  b = bs + local % nb;
-  return e;
-}
 
 // Row tables of block b: the token and pair of each row go to LDS; the
 // row's epilogue factors (stage-2 pair weight, A8W8 row scale) stay in the
@@ -155,100 +113,6 @@ __device__ __forceinline__ int lds_chunk_off(int r, int c) {
   return (c / 4) * 1024 + (c % 4) * 256 + ((r ^ c ^ ((r & 1) << 3)) & 15) * 16;
 }
 
-// Stage-2 pair rows in 16-bit block-scaled form.  The 64 values v of one
-// (pair, 64-column tile) become one 128-byte line of 16-bit words
-// 2 q + b: q = rint(v * 2^(14 - e)) saturated to +-16383, with e the frexp
-// exponent of the tile's largest magnitude (|v| < 2^e) raised to at least
-// -126, and b, the lowest bit of the words of columns 0..7, spelling the
-// 8-bit field e + 126 (255: the tile holds a non-finite value).  Each value
-// is held to within 2^-13 of the tile's largest magnitude, at half the bytes
-// of fp32, and every line is written once and read once, so no cache ever
-// holds a stale copy of it.  The words fill the first P*H*2 bytes of the pair
-// buffer.
-constexpr int kPairNonFinite = 255;
-
-__device__ __forceinline__ int16_t* pair_codes(const GemmParams& p) { return reinterpret_cast<int16_t*>(p.pair_out); }
-// Running largest magnitude of a tile that also records non-finite values:
-// a NaN or an infinity makes it +Inf for good (fmaxf alone would drop a NaN),
-// so the tile's field below becomes kPairNonFinite and its sum NaN.
-__device__ __forceinline__ float tile_amax(float amax, float v) {
-  const float m = fabsf(v);
-  return m <= 3.4028234664e38f ? fmaxf(amax, m) : __builtin_inff();
-}
-// The tile's 8-bit exponent field from its largest magnitude.
-__device__ __forceinline__ int pair_tile_field(float amax) {
-  if (!(amax <= 3.4028234664e38f)) return kPairNonFinite;  // Inf or NaN
-  int ex;
-  (void)__builtin_frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1); 0 for amax = 0
-  return (ex < -126 ? -126 : ex) + 126;
-}
-// Words of two values of columns col, col + 1 of the tile (low half first).
-__device__ __forceinline__ uint32_t pair_code2(float a, float b, int field, int col) {
-  const int sh = 14 - ((field == kPairNonFinite ? 0 : field) - 126);
-  int qa = (int)__builtin_rintf(__builtin_ldexpf(a, sh));
-  int qb = (int)__builtin_rintf(__builtin_ldexpf(b, sh));
-  qa = qa > 16383 ? 16383 : (qa < -16383 ? -16383 : qa);
-  qb = qb > 16383 ? 16383 : (qb < -16383 ? -16383 : qb);
-  const int ba = col < 8 ? (field >> col) & 1 : 0;
-  const int bb = col + 1 < 8 ? (field >> (col + 1)) & 1 : 0;
-  return ((uint32_t)(2 * qa + ba) & 0xFFFFu) | ((uint32_t)(2 * qb + bb) << 16);
-}
-
-// Stage-2 pair rows of the waves' last arrivals: the addend plus the token's
-// k_total pair rows in slot order (each q times its tile's power of two, an
-// exact product, added in fp32), one rounding.  Eight lanes share a token
-// (lane part c sums columns cbase + 8c .. + 7), so each load of a row reads
-// its 128-byte line whole; part 0 holds the exponent bits and passes the
-// field to the other seven.  Read with ordinary loads: every pair row of the
-// tile was written through this XCD's L2.
-__device__ __forceinline__ void last_arrival_sum8_xcd(const GemmParams& p, int tok, int cbase, int c, int lane) {
-  const int col = cbase + 8 * c;
-  float v[8];
-  if (p.acc) {
-    const float4 a0 = *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + col);
-    const float4 a1 = *reinterpret_cast<const float4*>(p.acc + (size_t)tok * p.H + col + 4);
-    v[0] = a0.x, v[1] = a0.y, v[2] = a0.z, v[3] = a0.w;
-    v[4] = a1.x, v[5] = a1.y, v[6] = a1.z, v[7] = a1.w;
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = 0.f;
-  }
-  const int16_t* rows = pair_codes(p) + (size_t)tok * p.k_total * p.H + col;
-  const int src = lane & ~7;  // part 0 of this token
-  auto add_row = [&](const uint4& t) {
-    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-    int field = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) field |= (int)((w[q] & 1u) << (2 * q)) | (int)(((w[q] >> 16) & 1u) << (2 * q + 1));
-    field = __shfl(field, src, kWave);
-    const float s = field == kPairNonFinite ? __builtin_nanf("") : __builtin_ldexpf(1.0f, field - 126 - 14);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] += (float)((int)(int16_t)(w[q] & 0xFFFFu) >> 1) * s;
-      v[2 * q + 1] += (float)((int)(int16_t)(w[q] >> 16) >> 1) * s;
-    }
-  };
-  int jj = 0;
-  for (; jj + 4 <= p.k_total; jj += 4) {
-    uint4 t[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) t[r] = *reinterpret_cast<const uint4*>(rows + (size_t)(jj + r) * p.H);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) add_row(t[r]);
-  }
-  for (; jj < p.k_total; ++jj) add_row(*reinterpret_cast<const uint4*>(rows + (size_t)jj * p.H));
-  if (p.out_bf16) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = f32_to_bf16(v[2 * q]) | (f32_to_bf16(v[2 * q + 1]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + (size_t)tok * p.H + col) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)tok * p.H + col);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
-}
-
 // One block b of expert view ev: this wave's columns start at c0 (stage 1: h
 // columns c0..c0+31; stage 2: output columns c0..c0+63); waves with
 // wave_ok = false take part in the staging and barriers but store nothing.
@@ -301,7 +165,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   const uint32_t kfrag32 = (uint32_t)(((lane / 32) * 16 + l16) * 16);
   const uint32_t wlane = k32 ? (uint32_t)(((lane % 32) / 16) * ev.nkt * 2048) + kfrag32 : (uint32_t)lane * 16;
 
-  int live = 0;  // live rows of the block (set once its row tables are read)
+  int live = 0;  // real rows of the block (set once its row tables are read)
 
   // ---- staged token rows: chunk q = tid + 256 u is chunk q % 8 of row q / 8;
   // padding rows read past the buffer ----
@@ -369,8 +233,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // token-row register sets in flight: XD = 2 keeps the rows of K tiles
   // kt + 1 and kt + 2 loading while tile kt is multiplied
   constexpr int XD =
-      (((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) || (FMT == FMT_A8W8 && STAGE == 2 && NB == 4) ||
-       NB == 16)
+      (((FMT == FMT_A8W8 || FMT == FMT_BF16) && STAGE == 1 && NB == 8) || (FMT == FMT_A8W8 && STAGE == 2 && NB == 4))
           ? 1
           : 2;
   uint4 xr[XD][CPT];
@@ -379,7 +242,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
-      xr[set][u] = (NB < 16 || 32 * u < live) ? tile_load16(xrs, xoff[u], (uint32_t)kt * 128) : make_uint4(0, 0, 0, 0);
+      xr[set][u] = tile_load16(xrs, xoff[u], (uint32_t)kt * 128);
     if constexpr (FMT == FMT_MX) {
       xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);  // tid >= BM: reads 0
     }
@@ -387,7 +250,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   auto store_x = [&](int buf, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      if (NB < 16 || 32 * u < live) *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
+      *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
     }
     if constexpr (FMT == FMT_MX) {
       sm.xsc[buf][tid < BM ? tid : BM] = xsr[set];  // no branch: the other threads write the spare slot
@@ -418,14 +281,12 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   // The multiply of a K tile runs at raised wave priority, so a wave with its
   // operands ready keeps the matrix core busy ahead of the SIMD's other wave
   // issuing loads (measured: a8w8 stage 1 -5 %, bf16 and MX unchanged).
-  // k32: four K steps of 16 over the live 32-row token groups; consecutive
-  // MFMAs update different accumulators
+  // k32: four K steps of 16; consecutive MFMAs update different accumulators
   auto compute_k32 = [&](int buf, const uint4 (&w)[4][2]) {
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
-        if (32 * nn >= live) continue;  // wave-uniform: a group of padding rows
         const uint4 bf = *reinterpret_cast<const uint4*>(&sm.x[buf][nn * 4096 + xf32(st)]);
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
@@ -436,7 +297,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   };
   auto compute = [&](int buf, const uint4 (&w)[4][2], const int (&sc)[4]) {
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (k32 && STAGE == 1 && NB <= 8) {
+    if constexpr (k32 && STAGE == 1) {
       {
         // four K steps of 16; the token fragments of step st + 1 are read
         // while step st multiplies (LDS latency behind eight MFMAs); the
@@ -472,7 +333,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if (NB == 16 && 16 * nb >= live) continue;  // wave-uniform: a group of padding rows
         const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo0]);
         const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo1]);
         const int sb = (FMT == FMT_MX) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
@@ -497,9 +357,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   load_w(wA, sA, 0);
   load_w(wB, sB, 1);
   float rw_row, rs_row;
-  // live rows: a block's real rows come first and its padding last, so the
-  // live rows are rows 0 .. live-1; the loads and multiplies of 32-row (16-row)
-  // groups past them are skipped (wave-uniform branches)
+  // a block's real rows come first and its padding last
   live = __syncthreads_count(tile_rows<FMT, STAGE, BM>(p, b, tid, sm.tok, sm.pair, rw_row, rs_row));
   if (live == 0) return;  // a block part holding only padding rows
   row_offsets();
@@ -857,7 +715,6 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 // for the 64-row a8w8 stage-2 items).
 template <int FMT, int STAGE, int NB>
 constexpr int tile_waves_per_eu() {
-  if (NB == 16) return 1;  // 256-row blocks: 256 accumulator registers per lane
   if (FMT == FMT_A8W8 && STAGE == 2 && NB == 4) return 3;  // with one token-row set in flight (a8w8 stage 2 -2 %)
   return (FMT == FMT_BF16 || NB <= 4 || (FMT == FMT_A8W8 && STAGE == 1)) ? 2 : 1;
 }
@@ -954,7 +811,7 @@ void gemm_tile_accum_kernel(GemmParams p) {
 // addressed with 32-bit buffer offsets.
 bool tile_kernel_fits(const GemmParams& p, int stage, int fmt) {
   if (fmt == FMT_F32) return false;
-  if (p.block_m != 32 && p.block_m != 64 && p.block_m != 128 && p.block_m != 256) return false;
+  if (p.block_m != 32 && p.block_m != 64 && p.block_m != 128) return false;
   const size_t esz = fmt == FMT_BF16 ? 2 : 1;
   const size_t hsz = fmt == FMT_A8W8 ? 2 : esz;
   if (stage == 1) {
@@ -992,7 +849,6 @@ static hipError_t launch_tile_fs(const GemmParams& p, hipStream_t s) {
     case 32: return launch_tile_nb<FMT, STAGE, 2>(p, s);
     case 64: return launch_tile_nb<FMT, STAGE, 4>(p, s);
     case 128: return launch_tile_nb<FMT, STAGE, 8>(p, s);
-    case 256: return launch_tile_nb<FMT, STAGE, 16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

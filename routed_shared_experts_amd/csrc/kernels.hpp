@@ -119,6 +119,8 @@ hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t
 bool wave_kernel_fits(const GemmParams& p, int stage, int fmt);
 hipError_t launch_gemm_tile(const GemmParams& p, int stage, int fmt, hipStream_t s);
 bool tile_kernel_fits(const GemmParams& p, int stage, int fmt);
+hipError_t launch_gemm_lds(const GemmParams& p, int stage, int fmt, hipStream_t s);
+bool lds_kernel_fits(const GemmParams& p, int stage, int fmt);
 hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes, hipStream_t s);
 hipError_t launch_pack_scales(const void* src, void* dst, int64_t rows, int32_t scale_bytes, hipStream_t s);
 
