@@ -29,9 +29,10 @@
  * Conventions for every entry point:
  * - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *   aligned, row-major and dense.  The library never allocates and never
- *   frees.  Its only mutable state is one thread-local slot holding the HIP
+ *   frees.  Its mutable state is one thread-local slot holding the HIP
  *   error behind the calling thread's last MOE_ERR_HIP (read with
- *   moe_last_hip_error); calls are otherwise stateless and reentrant.
+ *   moe_last_hip_error) and, for moe_forward_noalloc only, its per-device
+ *   scratch array; calls are otherwise stateless and reentrant.
  * - Every argument is validated on the host before anything is launched; an
  *   invalid call returns an error and launches nothing.  Launch failures
  *   return MOE_ERR_HIP; faults inside kernels surface at the caller's next
@@ -210,6 +211,27 @@ size_t moe_workspace_bytes(const moe_forward_args* a);
 moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_bytes,
                        hipStream_t main, hipStream_t aux, hipEvent_t ev_fork,
                        hipEvent_t ev_ready);
+
+/* Largest workspace moe_forward_noalloc provides (bytes). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library, one copy per GPU, held until the
+ * process ends; its address on the current device is looked up on the first
+ * call on that device (the library's only other state: a mutex-guarded table
+ * of those addresses).  Arguments and launch sequence as moe_forward; the
+ * streams and events must belong to the current device.  Returns
+ * MOE_ERR_WORKSPACE when moe_workspace_bytes(a) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (decode-sized batches fit: the workspace grows
+ * with T * (topk + shared chunks) * H), MOE_ERR_HIP if the look-up fails.
+ * Nothing is allocated.  Every call on a GPU shares that GPU's array, whose
+ * contents a call never relies on: two calls that overlap in time on one
+ * GPU (different streams, or the aux stream of one with the main stream of
+ * the other) race and give undefined results. */
+moe_status moe_forward_noalloc(const moe_forward_args* a, hipStream_t main, hipStream_t aux,
+                               hipEvent_t ev_fork, hipEvent_t ev_ready);
 
 /* ---- the individual steps (what moe_forward composes) ---------------- */
 

@@ -35,7 +35,7 @@ SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE
                 "auto": MOE_SHARED_AUTO}
 
 # Exported symbols, in the order of include/moe.h.
-EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_route", "shared_gate_dot",
+EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_route", "shared_gate_dot",
            "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_pack_weights", "moe_pack_mx_scales",
            "moe_sort_tokens", "moe_stage1", "moe_stage2_accum", "moe_query_feature", "moe_status_str",
            "moe_last_hip_error"]
@@ -91,6 +91,7 @@ def _load():
         "moe_workspace_bytes": (c_size_t, [P(MoeForwardArgs)]),
         "moe_forward": (c_int32, [P(MoeForwardArgs), c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                   c_void_p]),
+        "moe_forward_noalloc": (c_int32, [P(MoeForwardArgs), c_void_p, c_void_p, c_void_p, c_void_p]),
         "moe_route": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                 c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "shared_gate_dot": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -238,6 +239,20 @@ def moe_forward(args, workspace, main_stream=None, aux_stream=None, ev_fork=None
                           ctypes.c_void_p(ev_fork) if ev_fork else None,
                           ctypes.c_void_p(ev_ready) if ev_ready else None)
     _check(st, "moe_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/moe.h
+
+
+def moe_forward_noalloc(args, main_stream=None, aux_stream=None, ev_fork=None, ev_ready=None):
+    """Run the layer on the library's own per-device scratch (no workspace,
+    nothing allocated); raises MoeError with MOE_ERR_WORKSPACE when the
+    request needs more than MOE_NOALLOC_SCRATCH_BYTES."""
+    aux = ctypes.c_void_p(aux_stream.cuda_stream) if aux_stream is not None else None
+    st = _lib.moe_forward_noalloc(ctypes.byref(args), _stream(main_stream), aux,
+                                  ctypes.c_void_p(ev_fork) if ev_fork else None,
+                                  ctypes.c_void_p(ev_ready) if ev_ready else None)
+    _check(st, "moe_forward_noalloc")
 
 
 from .layer import (FORMATS, weights_struct, forward_args, pack_weights, MoeLayer)  # noqa: E402,F401

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
@@ -270,6 +272,44 @@ thread_local hipError_t g_last_hip = hipSuccess;  // last HIP failure reported a
 // that the hipGetLastError() after each launch here reports that launch.
 // (Errors from a faulted kernel are sticky and still surface.)
 inline void clear_pending_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+// ---- the allocation-free forward ------------------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the workspace lives in a
+// file-scope device array, one copy per GPU for the life of the process.  In
+// host code the array's name is only a stand-in; its device address on the
+// current GPU is looked up once per device and used from then on.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];  // device address of `scratch`, per device
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return MOE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return MOE_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -705,6 +745,19 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   }
   HIP_TRY(launch_gemm(g, 2, fmt, 64, main_s));
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_forward_args* a, hipStream_t main_s, hipStream_t aux_s,
+                               hipEvent_t ev_fork, hipEvent_t ev_ready) {
+  int fmt = -1;
+  const moe_status st = validate_impl(a, &fmt);
+  if (st != MOE_OK) return st;
+  if (a->T == 0) return MOE_OK;
+  if (make_plan(a, fmt).off_end > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const moe_status sst = scratch_of_current_device(&ws);
+  if (sst != MOE_OK) return sst;
+  return moe_forward(a, ws, MOE_NOALLOC_SCRATCH_BYTES, main_s, aux_s, ev_fork, ev_ready);
 }
 
 }  // extern "C"
