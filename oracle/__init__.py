@@ -24,9 +24,10 @@ discussions:
 
 Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
 
-* codecs (bf16, e4m3fn, e8m0, MX-32, per-row e4m3): pinned -- exhaustive code
-  tables vs the OCP closed form and torch's float8/bfloat16 casts, brute-force
-  nearest-code search, crafted MX blocks.
+* codecs (bf16, e4m3fn, e8m0, MX-32, per-row e4m3, e2m1 / MXFP4): pinned --
+  exhaustive code tables vs the OCP closed forms (the e2m1 table of the OCP MX
+  specification as a golden file) and torch's float8/bfloat16 casts,
+  brute-force nearest-code search, crafted MX blocks, the nibble order.
 * spec_exp / spec_sigmoid: pinned -- exact special values, <= 2 ulp against
   float64 on a dense sweep, monotonicity.
 * route: pinned -- definition checks on every token, exhaustive group-subset
@@ -54,6 +55,9 @@ from .codecs import (
     mx_quantize,
     mx_dequantize,
     row_quantize_e4m3,
+    e2m1_decode,
+    e2m1_unpack,
+    mx4_dequantize,
 )
 from .specmath import spec_exp, spec_sigmoid
 from .routing import route
@@ -70,7 +74,8 @@ from .layer import (
 
 __all__ = [
     "bf16_bits_to_f64", "round_to_bf16_bits", "e4m3_decode", "e4m3_encode_rne_sat",
-    "e8m0_decode", "mx_quantize", "mx_dequantize", "row_quantize_e4m3",
+    "e8m0_decode", "mx_quantize", "mx_dequantize", "row_quantize_e4m3", "e2m1_decode", "e2m1_unpack",
+    "mx4_dequantize",
     "spec_exp", "spec_sigmoid", "route", "sort_tokens", "gate",
     "decode_activations", "expert_weights", "shared_weights", "expert_mlp",
     "moe_layer", "stage1_reference",

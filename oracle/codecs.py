@@ -18,6 +18,13 @@ Formats:
   Shared exponent: floor(log2(amax)) - 8 (8 = the largest exponent of e4m3),
   clamped to [-127, 127]; elements are v * 2^-exponent rounded RNE to e4m3 and
   saturated to +-448.  An all-zero block gets scale byte 0 and zero codes.
+* e2m1 (OCP MX FP4): sign, 2 exponent bits with bias 1, 1 mantissa bit;
+  exponent field 0 encodes the subnormals 0 and 0.5; no infinity or NaN; the
+  largest value is 6.  Two elements per byte, element 2i in the low nibble of
+  byte i (the order the gfx950 block-scaled MFMA reads them in).  The pages
+  deploy MXFP4 expert weights (vLLM PR 65207, Purpose, commit 3: Quark MXFP4
+  checkpoints; SGLang PR 27057, Modifications, item 1) without restating the
+  format; MXFP4 = MX-32 blocks of e2m1 elements with an e8m0 scale.
 * per-row e4m3 (used for the stage-2 input in the a8w8 layer): one fp32 scale
   per row, s = amax / 448, codes = e4m3_rne_sat(v * (448 / amax)), both
   products in fp32; an all-zero row gets s = 1 and zero codes.  The pages name
@@ -104,6 +111,35 @@ def e4m3_encode_rne_sat(x):
     code = np.where(is_norm, code_norm, code_sub)
     code = code | (np.signbit(x).astype(np.int64) << 7)
     return code.astype(np.uint8)
+
+
+def e2m1_decode(codes):
+    """e2m1 codes (0..15) -> float64 by the closed form: (-1)^S * 2^(E-1) *
+    (1 + M/2) for E > 0, (-1)^S * M/2 for E = 0."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    v = np.where(e == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, e - 1))
+    return np.where(s == 1, -v, v)
+
+
+def e2m1_unpack(packed):
+    """Bytes [..., K/2] holding two e2m1 codes each -> codes [..., K]
+    (element 2i from the low nibble of byte i, 2i+1 from the high one)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def mx4_dequantize(scales, packed):
+    """MXFP4: (e8m0 scale bytes [..., K/32], packed e2m1 [..., K/2]) -> float64 [..., K]."""
+    vals = e2m1_decode(e2m1_unpack(packed))
+    K = vals.shape[-1]
+    blocks = vals.reshape(vals.shape[:-1] + (K // 32, 32))
+    return (blocks * e8m0_decode(scales)[..., None]).reshape(vals.shape)
 
 
 def e8m0_decode(b):

@@ -26,6 +26,8 @@ activation and the fused quantisation; MX GEMMs use 32-element K blocks):
 * fmt 'a8w8':  x e4m3 with an fp32 scale per token; W e4m3 with an fp32 scale
                per expert (one for W13, one for W2); h rounded to bf16 then
                quantised per row to e4m3 with an fp32 row scale.
+* fmt 'mxfp4': as 'mxfp8' (x and h MX-32 e4m3) with MXFP4 weights: e2m1
+               elements, an e8m0 scale per 32 K elements.
 
 Every dot product is float64 over the exactly decoded operands, so the only
 roundings are the quantisation points themselves.  The shared expert is
@@ -35,7 +37,7 @@ evaluated whole (intermediate width I_s), never split.
 import numpy as np
 
 from .codecs import (bf16_bits_to_f64, round_to_bf16_bits, e4m3_decode,
-                     mx_quantize, mx_dequantize, row_quantize_e4m3)
+                     mx_quantize, mx_dequantize, mx4_dequantize, row_quantize_e4m3)
 from .routing import route
 
 
@@ -56,7 +58,7 @@ def decode_activations(inp, fmt):
     T = x.shape[0]
     if fmt in ("f32", "bf16"):
         return _decode_plain(x, fmt), np.ones(T)
-    if fmt == "mxfp8":
+    if fmt in ("mxfp8", "mxfp4"):
         xf = bf16_bits_to_f64(x).astype(np.float32)
         sc, q = mx_quantize(xf)
         return mx_dequantize(sc, q), np.ones(T)
@@ -83,6 +85,8 @@ def _weights(w13, w2, s13, s2, fmt):
         return _decode_plain(w13, fmt), _decode_plain(w2, fmt), 1.0, 1.0
     if fmt == "mxfp8":
         return mx_dequantize(s13, w13), mx_dequantize(s2, w2), 1.0, 1.0
+    if fmt == "mxfp4":
+        return mx4_dequantize(s13, w13), mx4_dequantize(s2, w2), 1.0, 1.0
     if fmt == "a8w8":
         return e4m3_decode(w13), e4m3_decode(w2), float(np.float32(s13)), float(np.float32(s2))
     raise ValueError(fmt)
@@ -114,7 +118,7 @@ def quantize_h(h, fmt):
     hb = bf16_bits_to_f64(round_to_bf16_bits(h))
     if fmt == "bf16":
         return hb, np.ones(n)
-    if fmt == "mxfp8":
+    if fmt in ("mxfp8", "mxfp4"):
         sc, q = mx_quantize(hb.astype(np.float32))
         return mx_dequantize(sc, q), np.ones(n)
     if fmt == "a8w8":

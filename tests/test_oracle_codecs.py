@@ -146,3 +146,33 @@ def test_row_quantize():
     assert s[1] == 1.0 and np.array_equal(oracle.e4m3_decode(q[1, :8]), [448, -448, 1, 2, 3, 0.5, 96, -7])
     assert s[2] == np.float32(3.0) / np.float32(448)
     assert q[2, -1] == 0x7E
+
+
+def _golden_e2m1():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "e2m1_values.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            code, val = line.split()
+            rows.append((int(code, 2), float(val)))
+    return rows
+
+
+def test_e2m1_decode_matches_the_ocp_table():
+    rows = _golden_e2m1()
+    assert [c for c, _ in rows] == list(range(16))
+    got = oracle.e2m1_decode(np.arange(16))
+    want = np.array([v for _, v in rows])
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))  # -0.0 for code 1000
+
+
+def test_e2m1_unpack_nibble_order_and_mx4_scales():
+    # byte 0x21: element 0 = low nibble 0001 (0.5), element 1 = high nibble 0010 (1.0)
+    assert oracle.e2m1_unpack(np.array([0x21, 0xF7], np.uint8)).tolist() == [1, 2, 7, 15]
+    packed = np.tile(np.array([0x21], np.uint8), (2, 16))  # two rows of 32 elements
+    scales = np.array([[127], [130]], np.uint8)              # 2^0 and 2^3
+    v = oracle.mx4_dequantize(scales, packed)
+    assert v.shape == (2, 32)
+    assert np.array_equal(v[0], np.tile([0.5, 1.0], 16))
+    assert np.array_equal(v[1], np.tile([4.0, 8.0], 16))

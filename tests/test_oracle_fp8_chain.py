@@ -82,15 +82,29 @@ def _row_quant(v32):
     return q, torch.where(nz, s, torch.ones_like(s)).double()
 
 
+def _e2m1_table():
+    """The 16 e2m1 values from the OCP MX specification's table (golden file)."""
+    import os
+    vals = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            vals.append(float(line.split()[1]))
+    return torch.tensor(vals, dtype=torch.float64)
+
+
 def torch_expert(inp, fmt):
-    """One routed expert in fp8, from the definitions (no oracle code)."""
-    I = inp["w2"].shape[-1]
-    if fmt == "mxfp8":
+    """One routed expert in fp8 / MXFP4, from the definitions (no oracle code)."""
+    if fmt in ("mxfp8", "mxfp4"):
         x32 = torch.from_numpy(inp["x"].astype(np.uint32) << 16).view(torch.float32)
         x = _mx_quant(x32)
         sx = torch.ones(x.shape[0], dtype=torch.float64)
         def wdec(codes, sc):
-            v = _e4m3_values(codes)
+            if fmt == "mxfp8":
+                v = _e4m3_values(codes)
+            else:  # two e2m1 codes per byte, the even element in the low nibble
+                b = torch.from_numpy(np.ascontiguousarray(codes)).long()
+                v = torch.stack([_e2m1_table()[b & 15], _e2m1_table()[b >> 4]], dim=-1).reshape(b.shape[0], -1)
             ex = torch.from_numpy(sc.astype(np.int64) - 127).double()
             return v * torch.ldexp(torch.ones_like(v), ex.repeat_interleave(32, dim=-1))
         W13 = wdec(inp["w13"][0], inp["w13_scale"][0])
@@ -103,10 +117,11 @@ def torch_expert(inp, fmt):
         W2 = _e4m3_values(inp["w2"][0])
         s13 = float(inp["w13_scale"][0])
         s2 = float(inp["w2_scale"][0])
+    I = W2.shape[1]
     a = (x @ W13.T) * sx[:, None] * s13
     h = torch.nn.functional.silu(a[:, :I]) * a[:, I:]
     hb = _bf16(h)
-    if fmt == "mxfp8":
+    if fmt in ("mxfp8", "mxfp4"):
         hq, sh = _mx_quant(hb.float()), torch.ones(h.shape[0], dtype=torch.float64)
     else:
         hq, sh = _row_quant(hb.float())
@@ -123,13 +138,13 @@ def _compare(fmt):
     return np.abs(y - ref).max() / rms
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "a8w8"])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "a8w8"])
 def test_fp8_expert_chain_matches_independent_torch_reference(fmt):
     # the two differ only in the float64 summation order of the products
     assert _compare(fmt) <= 1e-12
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "a8w8"])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "a8w8"])
 def test_fp8_h_codes_match_independent_torch_reference(fmt):
     cfg = _cfg(fmt)
     inp = workloads.to_host(workloads.generate(cfg))
@@ -144,7 +159,7 @@ def _planted(monkeypatch, fmt, mistake):
     real = L.quantize_h
 
     def no_bf16(h, f):
-        if f == "mxfp8":
+        if f in ("mxfp8", "mxfp4"):
             sc, q = oracle.mx_quantize(h.astype(np.float32))
             return oracle.mx_dequantize(sc, q), np.ones(h.shape[0])
         s, q = oracle.row_quantize_e4m3(h.astype(np.float32))
@@ -161,7 +176,8 @@ def _planted(monkeypatch, fmt, mistake):
                                           "no_row_scale": no_row_scale}[mistake])
 
 
-@pytest.mark.parametrize("fmt,mistake", [("mxfp8", "no_bf16"), ("mxfp8", "no_quant"), ("a8w8", "no_bf16"),
+@pytest.mark.parametrize("fmt,mistake", [("mxfp8", "no_bf16"), ("mxfp8", "no_quant"), ("mxfp4", "no_bf16"),
+                                         ("mxfp4", "no_quant"), ("a8w8", "no_bf16"),
                                          ("a8w8", "no_quant"), ("a8w8", "no_row_scale")])
 def test_planted_oracle_mistakes_are_caught(monkeypatch, fmt, mistake):
     _planted(monkeypatch, fmt, mistake)

@@ -13,7 +13,7 @@ from oracle import layer as L
 
 def _small(fmt="f32", **kw):
     base = dict(name="pin", T=12, H=64, E=6, I=32, I_s=64, topk=2, fmt=fmt, logits="iid")
-    if fmt in ("mxfp8", "a8w8"):
+    if fmt in ("mxfp8", "mxfp4", "a8w8"):
         base.update(H=128, I=128, I_s=128, gated=False, score="sigmoid", n_group=2, topk_group=1)
     base.update(kw)
     return workloads.LayerConfig(**base)
@@ -64,7 +64,7 @@ def test_shared_expert_and_gate_match_torch():
     assert np.allclose(y, gamma[:, None] * s, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "mxfp8", "a8w8"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "mxfp8", "mxfp4", "a8w8"])
 def test_layer_equals_dense_brute_force(fmt):
     cfg = _small(fmt)
     inp = _inputs(cfg)

@@ -18,6 +18,8 @@ Workloads (the tiny one is small enough for the oracle to finish in seconds):
 * a8w8_large    T=8192, H=7168, E=256, I=2048, k=8, shared I_s=2048, sigmoid,
                 8 groups keep 4, e4m3 activations (fp32 per token) and weights
                 (fp32 per expert), Zipf(1.2) expert load, ungated
+* mxfp4, mxfp4_decode  the mxfp8 shape (T=512; T=32) with MXFP4 weights (e2m1
+                codes drawn at random, two per byte, e8m0 scale per 32)
 
 Zipf load uses the Gumbel-top-k construction (Kool, van Hoof & Welling 2019):
 logits[t, e] = ln p_{pi(e)} + G_te with G standard Gumbel, p_r proportional to
@@ -49,7 +51,7 @@ class LayerConfig:
     group_score_topk: int = 2
     renormalize: bool = True
     routed_scaling_factor: float = 1.0
-    fmt: str = "bf16"            # 'f32' | 'bf16' | 'mxfp8' | 'a8w8'
+    fmt: str = "bf16"            # 'f32' | 'bf16' | 'mxfp8' | 'mxfp4' | 'a8w8'
     gated: bool = True
     bias_std: float = 0.0
     logits: str = "iid"          # 'linear' | 'iid' | 'zipf'
@@ -79,6 +81,12 @@ CONFIGS = {
 }
 CONFIG_ORDER = ["tiny_f32", "decode_bf16", "prefill_bf16", "mxfp8", "a8w8_large"]
 
+# MXFP4 expert weights with MX-fp8 activations (the format the pages deploy,
+# vLLM PR 65207, Purpose, commit 3): the MXFP8 workload's shape with e2m1
+# weights, and a decode batch of it
+CONFIGS["mxfp4"] = CONFIGS["mxfp8"].replace(name="mxfp4", fmt="mxfp4")
+CONFIGS["mxfp4_decode"] = CONFIGS["mxfp8"].replace(name="mxfp4_decode", fmt="mxfp4", T=32)
+
 
 def _seed(*key):
     h = hashlib.sha256(repr((BASE_SEED,) + tuple(key)).encode()).digest()
@@ -107,15 +115,17 @@ def _weight_family(cfg, device, tag, n_mats, rows, cols, fmt):
         out = torch.empty(shape, dtype=torch.float32, device=device)
     elif fmt == "bf16":
         out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    elif fmt == "mxfp4":
+        out = torch.empty((n_mats, rows, cols // 2), dtype=torch.uint8, device=device)
     else:
         out = torch.empty(shape, dtype=torch.uint8, device=device)
     scales = None
-    if fmt == "mxfp8":
+    if fmt in ("mxfp8", "mxfp4"):
         scales = torch.empty((n_mats, rows, cols // 32), dtype=torch.uint8, device=device)
     elif fmt == "a8w8":
         scales = torch.empty((n_mats,), dtype=torch.float32, device=device)
     for e in range(n_mats):
-        r = _randn((rows, cols), device, cfg.name, tag, e)
+        r = _randn((rows, cols), device, cfg.name, tag, e) if fmt != "mxfp4" else None
         if fmt == "f32":
             out[e] = r.mul_(0.02)
         elif fmt == "bf16":
@@ -126,12 +136,29 @@ def _weight_family(cfg, device, tag, n_mats, rows, cols, fmt):
             g = _gen(device, cfg.name, tag + "_scale", e)
             scales[e] = torch.randint(116, 119, (rows, cols // 32), generator=g, device=device,
                                       dtype=torch.int32).to(torch.uint8)
+        elif fmt == "mxfp4":
+            # e2m1 codes 0..15 drawn from a fixed bell-shaped distribution over
+            # the magnitudes (0, 0.5, 1, 1.5, 2, 3, 4, 6) with a random sign, two
+            # per byte, and block exponents 2^-8 .. 2^-6: values of order 0.02
+            g = _gen(device, cfg.name, tag + "_codes", e)
+            mag = torch.multinomial(_E2M1_MAG_P.to(device), rows * cols, replacement=True, generator=g)
+            sign = torch.randint(0, 2, (rows * cols,), generator=g, device=device)
+            codes = (mag + 8 * sign).to(torch.uint8).view(rows, cols)
+            out[e] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+            g = _gen(device, cfg.name, tag + "_scale", e)
+            scales[e] = torch.randint(119, 122, (rows, cols // 32), generator=g, device=device,
+                                      dtype=torch.int32).to(torch.uint8)
         elif fmt == "a8w8":
             out[e] = _e4m3(r.mul_(64.0))
             g = _gen(device, cfg.name, tag + "_scale", e)
             u = torch.rand((1,), generator=g, device=device, dtype=torch.float32)
             scales[e] = (0.02 / 64.0) * (0.9 + 0.2 * u[0])
     return out, scales
+
+
+# probabilities of the e2m1 magnitude codes 0..7 (values 0, 0.5, 1, 1.5, 2,
+# 3, 4, 6) for random MXFP4 weights: a bell over the grid
+_E2M1_MAG_P = torch.tensor([0.10, 0.20, 0.20, 0.16, 0.14, 0.11, 0.06, 0.03], dtype=torch.float64)
 
 
 def _zipf_logits(cfg, device):
@@ -156,7 +183,7 @@ def generate(cfg, device="cpu"):
     xr = _randn((T, H), device, cfg.name, "x")
     if cfg.fmt == "f32":
         inp["x"] = xr
-    elif cfg.fmt in ("bf16", "mxfp8"):
+    elif cfg.fmt in ("bf16", "mxfp8", "mxfp4"):
         inp["x"] = xr.to(torch.bfloat16)
     else:  # a8w8: e4m3 codes ~ N(0, 100^2) and a per-token fp32 scale near 1/100
         inp["x"] = _e4m3(xr.mul_(100.0))
@@ -184,8 +211,9 @@ def generate(cfg, device="cpu"):
         ws13, s13 = _weight_family(cfg, device, "ws13", 1, 2 * I_s, H, cfg.fmt)
         ws2, s2 = _weight_family(cfg, device, "ws2", 1, H, I_s, cfg.fmt)
         inp["ws13"], inp["ws2"] = ws13[0], ws2[0]
-        inp["ws13_scale"] = None if s13 is None else (s13[0] if cfg.fmt == "mxfp8" else s13)
-        inp["ws2_scale"] = None if s2 is None else (s2[0] if cfg.fmt == "mxfp8" else s2)
+        mx = cfg.fmt in ("mxfp8", "mxfp4")
+        inp["ws13_scale"] = None if s13 is None else (s13[0] if mx else s13)
+        inp["ws2_scale"] = None if s2 is None else (s2[0] if mx else s2)
     else:
         inp["ws13"] = inp["ws2"] = inp["ws13_scale"] = inp["ws2_scale"] = None
     return inp
@@ -242,5 +270,5 @@ def zipf_expected_share(E, s):
 
 
 def bytes_per_weight(fmt):
-    return {"f32": 4.0, "bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32.0, "a8w8": 1.0}[fmt]
+    return {"f32": 4.0, "bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32.0, "mxfp4": 0.5 + 1.0 / 32.0, "a8w8": 1.0}[fmt]
 
