@@ -30,8 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s and achieved TFLOPS (% MFMA peak) / GB/s (% HBM) on 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "a8w8": 5000.0}
-DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "a8w8": "fp8-e4m3"}
+# mxfp4: e2m1 weights against e4m3 activations run at the fp8 rate
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0, "mxfp4": 5000.0, "a8w8": 5000.0}
+DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "mxfp4": "mxfp4-e2m1-w/mxfp8-a",
+              "a8w8": "fp8-e4m3"}
 TIMING_EVERY = 8
 N_EVENTS = 7  # timing events the layer takes (prologue and sort spans, each GEMM kernel's start and end)
 # sources of the GEMM kernels: a traffic figure in profiles/ holds only while
@@ -97,8 +99,8 @@ def algorithmic(cfg, ids, m_pseudo):
     the shared expert's rows count in the stages when it runs as pseudo-experts)."""
     import workloads
     bw = workloads.bytes_per_weight(cfg.fmt)
-    bx = {"f32": 4, "bf16": 2, "mxfp8": 2, "a8w8": 1}[cfg.fmt]
-    bh = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32, "a8w8": 1}[cfg.fmt]
+    bx = {"f32": 4, "bf16": 2, "mxfp8": 2, "mxfp4": 2, "a8w8": 1}[cfg.fmt]
+    bh = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32, "mxfp4": 1 + 1 / 32, "a8w8": 1}[cfg.fmt]
     bo = 4 if cfg.fmt == "f32" else 2
     T, H, I, Is, k = cfg.T, cfg.H, cfg.I, cfg.I_s, cfg.topk
     P = T * k

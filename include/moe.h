@@ -50,7 +50,13 @@
  *   A8W8 : x FP8_E4M3 + fp32 per-row (token) scale, weights FP8_E4M3 + fp32
  *          per-expert scale (one for W13, one for W2), h per-row e4m3 with an
  *          fp32 row scale (from bf16-rounded h)
- * FP8_E4M3 is the OCP e4m3fn format (max 448, no infinities).
+ *   MXFP4: as MXFP8 with FP4_E2M1 weights + MX32 e8m0 scales (the MXFP4
+ *          checkpoints of vLLM PR 65207, "Purpose", commit 3); H, I and I_s
+ *          multiples of 256; sorted blocks of at most 128 rows
+ * FP8_E4M3 is the OCP e4m3fn format (max 448, no infinities).  FP4_E2M1 is
+ * the OCP MX FP4 element (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives),
+ * two per byte, the element of even index in the low nibble: a weight row of
+ * K elements is K / 2 bytes.
  *
  * Weight layout: W13 is [n][2*I][H] with the I gate rows first and the I up
  * rows second; W2 is [n][H][I].  Products are x . W^T.  MX32 scales are e8m0
@@ -75,7 +81,7 @@ typedef enum {
   MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype;
 
 typedef enum {
   MOE_SCALE_NONE = 0,
@@ -102,7 +108,8 @@ typedef enum {
   MOE_FEATURE_MXFP8 = 4,
   MOE_FEATURE_A8W8 = 5,
   MOE_FEATURE_F32 = 6,
-  MOE_FEATURE_BF16 = 7
+  MOE_FEATURE_BF16 = 7,
+  MOE_FEATURE_MXFP4 = 8
 } moe_feature;
 
 /* Weight layout.  Logically every weight matrix is row-major: rows = output
@@ -117,6 +124,8 @@ typedef enum {
  * q (0..3) of tile row r at q * 16 + r.  Matrices of consecutive experts stay
  * consecutive (a tiled [n][rows][row_bytes] array is n tiled matrices back to
  * back), and a 16-row-aligned row range stays a contiguous byte range.
+ * FP4_E2M1 rows go through the same byte tiling: each 1 KiB half of a tile is
+ * then one 128-element K step in operand order.
  * moe_pack_weights / moe_pack_mx_scales convert once, at load time. */
 typedef enum {
   MOE_LAYOUT_ROW_MAJOR = 0, /* accepted only by the pack functions */

@@ -22,14 +22,14 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 # ---- enums (values fixed by include/moe.h) ----
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
 MOE_SCALE_NONE, MOE_SCALE_PER_ROW, MOE_SCALE_PER_EXPERT, MOE_SCALE_MX32 = 0, 1, 2, 3
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_SHARED_NONE, MOE_SHARED_PSEUDO, MOE_SHARED_AUX, MOE_SHARED_AUTO = 0, 1, 2, 3
 MOE_STAGE2_STORE, MOE_STAGE2_ACCUMULATE = 0, 1
 MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_TILED = 0, 1
 (MOE_FEATURE_ACCUMULATE_OUTPUT, MOE_FEATURE_PSEUDO_SHARED, MOE_FEATURE_AUX_STREAM,
- MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16) = 1, 2, 3, 4, 5, 6, 7
+ MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16, MOE_FEATURE_MXFP4) = 1, 2, 3, 4, 5, 6, 7, 8
 
 SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE_SHARED_AUX,
                 "auto": MOE_SHARED_AUTO}

@@ -26,17 +26,21 @@ int weights_fmt(const moe_weights& w) {
   if (w.dtype == MOE_BF16 && w.scale == MOE_SCALE_NONE) return FMT_BF16;
   if (w.dtype == MOE_FP8_E4M3 && w.scale == MOE_SCALE_MX32) return FMT_MX;
   if (w.dtype == MOE_FP8_E4M3 && w.scale == MOE_SCALE_PER_EXPERT) return FMT_A8W8;
+  if (w.dtype == MOE_FP4_E2M1 && w.scale == MOE_SCALE_MX32) return FMT_MX4;
   return -1;
 }
 
 int ktile_elems(int fmt) { return fmt == FMT_F32 ? 32 : (fmt == FMT_BF16 ? 64 : 128); }
-int h_elem_bytes(int fmt) { return fmt == FMT_F32 ? 4 : (fmt == FMT_MX ? 1 : 2); }
+
+// MXFP4 weight rows pack whole 128-byte tiles (256 e2m1 elements)
+bool mx4_shapes_ok(long long H, long long I, long long Is) { return H % 256 == 0 && I % 256 == 0 && Is % 256 == 0; }
+int h_elem_bytes(int fmt) { return fmt == FMT_F32 ? 4 : (fmt_mx(fmt) ? 1 : 2); }
 
 bool weights_ok(const moe_weights& w, int fmt) {
   if (!w.w13 || !w.w2 || !aligned16(w.w13) || !aligned16(w.w2)) return false;
-  if (fmt == FMT_MX || fmt == FMT_A8W8) {
+  if (fmt_mx(fmt) || fmt == FMT_A8W8) {
     if (!w.w13_scale || !w.w2_scale) return false;
-    if (fmt == FMT_MX && (((uintptr_t)w.w13_scale & 3u) || ((uintptr_t)w.w2_scale & 3u))) return false;
+    if (fmt_mx(fmt) && (((uintptr_t)w.w13_scale & 3u) || ((uintptr_t)w.w2_scale & 3u))) return false;
     if (fmt == FMT_A8W8 && (((uintptr_t)w.w13_scale & 3u) || ((uintptr_t)w.w2_scale & 3u))) return false;
   }
   return true;
@@ -90,6 +94,7 @@ int resolve_mode(const moe_forward_args* a, int fmt);
 // stages must fit them (whole 128-column stage-1 workgroups, 32-column pseudo
 // chunks, 32-bit buffer offsets).
 bool big_blocks_fit(const moe_forward_args* a, int fmt) {
+  if (fmt == FMT_MX4) return false;
   const int m = resolve_mode(a, fmt) == MOE_SHARED_PSEUDO ? (a->I_s + a->I - 1) / a->I : 0;
   const size_t esz = fmt == FMT_BF16 ? 2 : 1, hsz = fmt == FMT_A8W8 ? 2 : esz;
   if (a->I % 128 || (m > 0 && a->I_s % 32)) return false;
@@ -127,7 +132,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (const moe_status st = layout_status(a->routed)) return st;
   // activation format must match the weight format
   if (fmt == FMT_F32 && a->x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  if ((fmt == FMT_BF16 || fmt == FMT_MX) && a->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((fmt == FMT_BF16 || fmt_mx(fmt)) && a->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (fmt == FMT_A8W8) {
     if (a->x_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
     if ((a->T > 0 && !a->x_row_scale) || ((uintptr_t)a->x_row_scale & 3u)) return MOE_ERR_INVALID_ARG;
@@ -137,6 +142,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   const int kt = ktile_elems(fmt);
   if (a->H % kt || a->I % kt || (a->I_s % kt)) return MOE_ERR_INVALID_ARG;
   if (a->H % 64) return MOE_ERR_INVALID_ARG;  // stage-2 column tile
+  if (fmt == FMT_MX4 && !mx4_shapes_ok(a->H, a->I, a->I_s)) return MOE_ERR_INVALID_ARG;
   if (a->gate_w) {
     if (!aligned16(a->gate_w)) return MOE_ERR_INVALID_ARG;
     if (fmt != FMT_F32 && fmt != FMT_BF16) return MOE_ERR_UNSUPPORTED;
@@ -204,8 +210,8 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_ids = take((size_t)P * 4);
   pl.off_w = take((size_t)P * 4);
   pl.off_gamma = take((size_t)a->T * 4);
-  pl.off_xq = take(fmt == FMT_MX ? (size_t)a->T * a->H : 0);
-  pl.off_xs = take(fmt == FMT_MX ? (size_t)a->T * (a->H / 32) : 0);
+  pl.off_xq = take(fmt_mx(fmt) ? (size_t)a->T * a->H : 0);
+  pl.off_xs = take(fmt_mx(fmt) ? (size_t)a->T * (a->H / 32) : 0);
   pl.off_counts = take((size_t)pl.E_total * 4);
   pl.off_offsets = take((size_t)(pl.E_total + 1) * 4);
   pl.off_nblk = take(16);
@@ -213,11 +219,11 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   pl.off_sortws = take(sort_scratch_bytes((int)P, pl.E_total));
   pl.off_bexp = take((size_t)pl.max_blocks * 4);
   pl.off_h = take((size_t)pl.h_rows * a->I * esz_h);
-  pl.off_hs = take(fmt == FMT_MX ? (size_t)pl.h_rows * (a->I / 32) : 0);
+  pl.off_hs = take(fmt_mx(fmt) ? (size_t)pl.h_rows * (a->I / 32) : 0);
   const size_t dense_rows = (size_t)pl.dense_blocks * pl.dense_bm;
   const bool aux = pl.mode == MOE_SHARED_AUX;
   pl.off_hsh = take(aux ? dense_rows * a->I_s * esz_h : 0);
-  pl.off_hshs = take(aux && fmt == FMT_MX ? dense_rows * (a->I_s / 32) : 0);
+  pl.off_hshs = take(aux && fmt_mx(fmt) ? dense_rows * (a->I_s / 32) : 0);
   pl.amax_sh_bytes = aux && fmt == FMT_A8W8 ? align_up(dense_rows * 4, kAlign) : 0;
   pl.off_amax_sh = take(pl.amax_sh_bytes);
   // the addend (AUX mode only) and the per-pair stage-2 rows
@@ -337,6 +343,7 @@ int32_t moe_query_feature(int32_t feature) {
     case MOE_FEATURE_PSEUDO_SHARED:
     case MOE_FEATURE_AUX_STREAM:
     case MOE_FEATURE_MXFP8:
+    case MOE_FEATURE_MXFP4:
     case MOE_FEATURE_A8W8:
     case MOE_FEATURE_F32:
     case MOE_FEATURE_BF16: return 1;
@@ -507,8 +514,9 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   if (a->dense && a->max_blocks * a->block_m < a->T) return MOE_ERR_INVALID_ARG;
   const int kt = ktile_elems(fmt);
   if (a->H % kt || a->H % 64 || a->I % kt || a->I_s % kt) return MOE_ERR_INVALID_ARG;
+  if (fmt == FMT_MX4 && (a->block_m == 256 || !mx4_shapes_ok(a->H, a->I, a->I_s))) return MOE_ERR_INVALID_ARG;
   if (!a->x || !a->h || !aligned16(a->x) || !aligned16(a->h)) return MOE_ERR_INVALID_ARG;
-  if ((fmt == FMT_MX || fmt == FMT_A8W8) && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
+  if ((fmt_mx(fmt) || fmt == FMT_A8W8) && (!a->x_scale || !a->h_scale)) return MOE_ERR_INVALID_ARG;
   g = GemmParams{};
   g.T = a->T;
   g.H = a->H;
@@ -633,8 +641,8 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   const bool gated = a->gate_w != nullptr && a->I_s > 0;
   rp.gate_w = gated ? a->gate_w : nullptr;
   rp.gamma_out = gated ? gamma : nullptr;
-  rp.xq = fmt == FMT_MX ? xq : nullptr;
-  rp.xs = fmt == FMT_MX ? xs : nullptr;
+  rp.xq = fmt_mx(fmt) ? xq : nullptr;
+  rp.xs = fmt_mx(fmt) ? xs : nullptr;
   rp.do_route = 1;
 
   // sort (+ clearing of the accumulator unless the addend fills it)
@@ -675,8 +683,8 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.n_pseudo = pl.m;
   g.k_total = pl.k_total;
   fill_weights(g, a->routed, a->shared);
-  const void* x_stage = fmt == FMT_MX ? static_cast<const void*>(xq) : a->x;
-  const void* xs_stage = fmt == FMT_MX ? static_cast<const void*>(xs)
+  const void* x_stage = fmt_mx(fmt) ? static_cast<const void*>(xq) : a->x;
+  const void* xs_stage = fmt_mx(fmt) ? static_cast<const void*>(xs)
                                        : (fmt == FMT_A8W8 ? static_cast<const void*>(a->x_row_scale) : nullptr);
   g.x = static_cast<const uint8_t*>(x_stage);
   g.x_s = xs_stage;
@@ -695,7 +703,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
     gs.max_blocks = pl.dense_blocks;
     gs.h = ws + pl.off_hsh;
     gs.ld_h = a->I_s;
-    if (fmt == FMT_MX) gs.h_s = ws + pl.off_hshs;
+    if (fmt_mx(fmt)) gs.h_s = ws + pl.off_hshs;
     if (fmt == FMT_A8W8) {
       gs.h_s = ws + pl.off_amax_sh;
       HIP_TRY(zero_async(gs.h_s, pl.amax_sh_bytes, aux_s));
@@ -725,7 +733,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.offsets = pl.self_sort ? nullptr : offsets;
   g.h = ws + pl.off_h;
   g.ld_h = a->I;
-  g.h_s = fmt == FMT_MX ? static_cast<void*>(ws + pl.off_hs)
+  g.h_s = fmt_mx(fmt) ? static_cast<void*>(ws + pl.off_hs)
                         : (fmt == FMT_A8W8 ? static_cast<void*>(ws + pl.off_amax) : nullptr);
   if (tev) {
     g.ev_start = tev[3];

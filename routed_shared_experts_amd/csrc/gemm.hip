@@ -397,6 +397,7 @@ hipError_t launch_gemm(const GemmParams& p, int stage, int fmt, int bn, hipStrea
     }
     return launch_gemm_tile(p, stage, fmt, s);
   }
+  if (fmt == FMT_MX4) return hipErrorInvalidValue;  // e2m1 weights: one-wave and tiled kernels only
   return stage == 1 ? launch_stage<1>(p, fmt, bn, s) : launch_stage<2>(p, fmt, bn, s);
 }
 

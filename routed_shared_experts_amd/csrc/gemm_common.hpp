@@ -11,16 +11,27 @@
 
 namespace moe {
 
+// esz: bytes per activation (and stage-2 input) element in the MFMA K order;
+// wtile: bytes of one weight tile (16 rows x one K tile: 128 bytes of
+// activation per row; MXFP4 weights pack that K range in 64 bytes)
 template <int FMT>
 struct FmtInfo;
 template <>
-struct FmtInfo<FMT_F32> { static constexpr int esz = 4; static constexpr bool fp8 = false; };
+struct FmtInfo<FMT_F32> { static constexpr int esz = 4, wtile = 2048; static constexpr bool fp8 = false; };
 template <>
-struct FmtInfo<FMT_BF16> { static constexpr int esz = 2; static constexpr bool fp8 = false; };
+struct FmtInfo<FMT_BF16> { static constexpr int esz = 2, wtile = 2048; static constexpr bool fp8 = false; };
 template <>
-struct FmtInfo<FMT_MX> { static constexpr int esz = 1; static constexpr bool fp8 = true; };
+struct FmtInfo<FMT_MX> { static constexpr int esz = 1, wtile = 2048; static constexpr bool fp8 = true; };
 template <>
-struct FmtInfo<FMT_A8W8> { static constexpr int esz = 1; static constexpr bool fp8 = true; };
+struct FmtInfo<FMT_A8W8> { static constexpr int esz = 1, wtile = 2048; static constexpr bool fp8 = true; };
+template <>
+struct FmtInfo<FMT_MX4> { static constexpr int esz = 1, wtile = 1024; static constexpr bool fp8 = true; };
+
+// Bytes of a weight matrix region of `rows` rows with K elements each.
+template <int FMT>
+__device__ __forceinline__ size_t wbytes(size_t rows, size_t K) {
+  return rows * K * FmtInfo<FMT>::esz * FmtInfo<FMT>::wtile / 2048;
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
@@ -49,6 +60,12 @@ __device__ __forceinline__ void mfma_tile(f32x4& acc, const uint4& a0, const uin
                                                   acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1),
                                                   acc, 0, 0, 0);
+  } else if constexpr (FMT == FMT_MX4) {
+    // A: e2m1 weights, lane (g, r) holding K 32 g .. 32 g + 31 of row r in a0
+    // (even elements in low nibbles; a1 unused); B: e4m3 as for FMT_MX
+    i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+    i32x8 B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 0, 0, sa, 0, sb);
   } else {
     i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     i32x8 B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
@@ -57,9 +74,10 @@ __device__ __forceinline__ void mfma_tile(f32x4& acc, const uint4& a0, const uin
 }
 
 // Per-block problem description resolved from the expert index.  Weights
-// and MX scales are in the tiled layout (16-row x 128-byte tiles of 2048
-// bytes, row block major; 64-byte scale tiles), so a view is the base of its
-// row block 0 plus the tile count of a full matrix row and a first K tile.
+// and MX scales are in the tiled layout (16-row tiles of one K tile each,
+// 2048 bytes, or 1024 for MXFP4 weights; row block major; 64-byte scale
+// tiles), so a view is the base of its row block 0 plus the tile count of a
+// full matrix row, a first K tile and the tile size.
 struct ExpertView {
   const uint8_t* wa;   // stage 1: gate rows; stage 2: W2 rows
   const uint8_t* wb;   // stage 1: up rows
@@ -68,12 +86,13 @@ struct ExpertView {
   int nkt;             // K tiles per row of the underlying matrix
   int kt0;             // first K tile of this view (shared W2 pseudo-expert chunk)
   int width;           // stage 1: valid h columns; stage 2: valid K (h columns)
+  int tb;              // bytes of one weight tile
   float wscale;        // A8W8 per-expert scale
 };
 
 // Byte offset of tile (row block rb, K tile kt) of a view, and of its scales.
 __device__ __forceinline__ size_t tile_off(const ExpertView& v, int rb, int kt) {
-  return ((size_t)rb * v.nkt + v.kt0 + kt) * 2048;
+  return ((size_t)rb * v.nkt + v.kt0 + kt) * v.tb;
 }
 __device__ __forceinline__ size_t scale_tile_off(const ExpertView& v, int rb, int kt) {
   return ((size_t)rb * v.nkt + v.kt0 + kt) * 64;
@@ -84,23 +103,24 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
   constexpr int esz = FmtInfo<FMT>::esz;
   ExpertView v{};
   v.wscale = 1.0f;
+  v.tb = FmtInfo<FMT>::wtile;
   const int H = p.H, I = p.I, Is = p.I_s;
   if (e >= 0 && e < p.E) {
     if (STAGE == 1) {
-      v.wa = p.w13 + (size_t)e * 2 * I * H * esz;
-      v.wb = v.wa + (size_t)I * H * esz;
+      v.wa = p.w13 + wbytes<FMT>((size_t)e * 2 * I, H);
+      v.wb = v.wa + wbytes<FMT>(I, H);
       v.nkt = H * esz / 128;
       v.width = I;
-      if (FMT == FMT_MX) {
+      if (fmt_mx(FMT)) {
         v.sa = static_cast<const uint8_t*>(p.w13_s) + (size_t)e * 2 * I * (H / 32);
         v.sb = v.sa + (size_t)I * (H / 32);
       }
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w13_s)[e];
     } else {
-      v.wa = p.w2 + (size_t)e * H * I * esz;
+      v.wa = p.w2 + wbytes<FMT>((size_t)e * H, I);
       v.nkt = I * esz / 128;
       v.width = I;
-      if (FMT == FMT_MX) v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
+      if (fmt_mx(FMT)) v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w2_s)[e];
     }
   } else {
@@ -110,11 +130,11 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
     const int w = (e < 0) ? Is : min(I, Is - col0);
     if (STAGE == 1) {
       // rows col0.. of the gate and up halves (col0 is a multiple of 16)
-      v.wa = p.ws13 + (size_t)col0 * H * esz;
-      v.wb = p.ws13 + (size_t)(Is + col0) * H * esz;
+      v.wa = p.ws13 + wbytes<FMT>(col0, H);
+      v.wb = p.ws13 + wbytes<FMT>(Is + col0, H);
       v.nkt = H * esz / 128;
       v.width = w;
-      if (FMT == FMT_MX) {
+      if (fmt_mx(FMT)) {
         v.sa = static_cast<const uint8_t*>(p.ws13_s) + (size_t)col0 * (H / 32);
         v.sb = static_cast<const uint8_t*>(p.ws13_s) + (size_t)(Is + col0) * (H / 32);
       }
@@ -125,7 +145,7 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
       v.nkt = Is * esz / 128;
       v.kt0 = col0 * esz / 128;
       v.width = w;
-      if (FMT == FMT_MX) v.sa = static_cast<const uint8_t*>(p.ws2_s);
+      if (fmt_mx(FMT)) v.sa = static_cast<const uint8_t*>(p.ws2_s);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws2_s)[0];
     }
   }

@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kLdsThreads) void gemm_lds_accum_kernel(GemmParams 
 // (and 32-column-aligned pseudo chunks), stage 2 ACCUMULATE 64-column tiles;
 // 32-bit buffer offsets for the token rows.
 bool lds_kernel_fits(const GemmParams& p, int stage, int fmt) {
-  if (fmt == FMT_F32 || p.dense || p.block_m != kLdsBM || p.bsplit > 1) return false;
+  if (fmt == FMT_F32 || fmt == FMT_MX4 || p.dense || p.block_m != kLdsBM || p.bsplit > 1) return false;
   const size_t esz = fmt == FMT_BF16 ? 2 : 1;
   const size_t hsz = fmt == FMT_A8W8 ? 2 : esz;
   if (stage == 1) {

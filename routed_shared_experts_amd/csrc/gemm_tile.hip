@@ -143,7 +143,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   uint32_t wtile[4], stile[4];
   wrs[0] = tile_rsrc(ev.wa, 0x7FFFFFFF);
   wrs[1] = tile_rsrc((STAGE == 1) ? ev.wb : ev.wa, 0x7FFFFFFF);
-  if constexpr (FMT == FMT_MX) {
+  if constexpr (fmt_mx(FMT)) {
     srs[0] = tile_rsrc(ev.sa, 0x7FFFFFFF);
     srs[1] = tile_rsrc((STAGE == 1) ? ev.sb : ev.sa, 0x7FFFFFFF);
   }
@@ -172,11 +172,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
   __amdgpu_buffer_rsrc_t xrs, xsrs;
   if (STAGE == 1) {
     xrs = tile_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * esz));
-    if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
+    if constexpr (fmt_mx(FMT)) xsrs = tile_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
   } else {
     const size_t rows = (size_t)p.max_blocks * BM;
     xrs = tile_rsrc(p.h, (uint32_t)(rows * h_row_bytes<FMT>(p)));
-    if constexpr (FMT == FMT_MX) xsrs = tile_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
+    if constexpr (fmt_mx(FMT)) xsrs = tile_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
   }
   // LDS offset of chunk u: row tid / 8 + 32 u sits two 16-row fragments
   // (4 KiB) further on per u, with the same swizzle
@@ -199,7 +199,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
         xoff[u] = (uint32_t)(((size_t)b * BM + r) * h_row_bytes<FMT>(p)) + c * 16;
       }
     }
-    if (FMT == FMT_MX && tid < BM && sm.tok[tid] >= 0)
+    if (fmt_mx(FMT) && tid < BM && sm.tok[tid] >= 0)
       xsoff = (STAGE == 1) ? (uint32_t)(sm.tok[tid] * (p.H / 32)) : (uint32_t)((b * BM + tid) * (p.ld_h / 32));
   };
 
@@ -210,7 +210,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const __amdgpu_buffer_rsrc_t r = wrs[(STAGE == 1) ? mm : 0];
-        const uint32_t so = wtile[mm] + (uint32_t)kt * 2048;
+        const uint32_t so = wtile[mm] + (uint32_t)(kt * ev.tb);
 #pragma unroll
         for (int st = 0; st < 4; ++st) w[2 * mm + st / 2][st % 2] = tile_load16(r, wlane + 512 * st, so);
         sc[2 * mm] = sc[2 * mm + 1] = 127;
@@ -220,10 +220,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const __amdgpu_buffer_rsrc_t r = wrs[mb >> 1];
-      const uint32_t so = wtile[mb] + (uint32_t)kt * 2048;
+      const uint32_t so = wtile[mb] + (uint32_t)(kt * ev.tb);
       w[mb][0] = tile_load16(r, wlane, so);
-      w[mb][1] = tile_load16(r, wlane + 1024, so);
-      if constexpr (FMT == FMT_MX)
+      // MXFP4: one 1 KiB half per tile (lane (g, r): 32 e2m1 values)
+      w[mb][1] = FMT == FMT_MX4 ? make_uint4(0, 0, 0, 0) : tile_load16(r, wlane + 1024, so);
+      if constexpr (fmt_mx(FMT))
         sc[mb] = (int)__builtin_amdgcn_raw_buffer_load_b8(srs[mb >> 1], (int)lane, (int)(stile[mb] + kt * 64), 0);
       else
         sc[mb] = 127;
@@ -243,7 +244,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
     for (int u = 0; u < CPT; ++u)
       xr[set][u] = tile_load16(xrs, xoff[u], (uint32_t)kt * 128);
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (fmt_mx(FMT)) {
       xsr[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xsrs, (int)xsoff, kt * 4, 0);  // tid >= BM: reads 0
     }
   };
@@ -252,7 +253,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
     for (int u = 0; u < CPT; ++u) {
       *reinterpret_cast<uint4*>(&sm.x[buf][soff + 4096 * u]) = xr[set][u];
     }
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (fmt_mx(FMT)) {
       sm.xsc[buf][tid < BM ? tid : BM] = xsr[set];  // no branch: the other threads write the spare slot
     }
   };
@@ -335,7 +336,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       for (int nb = 0; nb < NB; ++nb) {
         const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo0]);
         const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.x[buf][nb * 2048 + xo1]);
-        const int sb = (FMT == FMT_MX) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
+        const int sb = (fmt_mx(FMT)) ? (int)((sm.xsc[buf][nb * 16 + l16] >> (8 * g)) & 0xFFu) : 127;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) mfma_tile<FMT>(acc[mb][nb], w[mb][0], w[mb][1], b0, b1, sc[mb], sb);
       }
@@ -428,7 +429,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int v = 0; v < 4; ++v) hv[m][v] = silu_mul(acc[m][nb][v] * sc, acc[m + 2][nb][v] * sc);
-      if constexpr (FMT == FMT_MX) {
+      if constexpr (fmt_mx(FMT)) {
         // the wave's 32 columns are one MX-32 block of the token's h row
         float amax = 0.f;
 #pragma unroll
@@ -857,6 +858,7 @@ hipError_t launch_gemm_tile(const GemmParams& p, int stage, int fmt, hipStream_t
   switch (fmt) {
     case FMT_BF16: return stage == 1 ? launch_tile_fs<FMT_BF16, 1>(p, s) : launch_tile_fs<FMT_BF16, 2>(p, s);
     case FMT_MX: return stage == 1 ? launch_tile_fs<FMT_MX, 1>(p, s) : launch_tile_fs<FMT_MX, 2>(p, s);
+    case FMT_MX4: return stage == 1 ? launch_tile_fs<FMT_MX4, 1>(p, s) : launch_tile_fs<FMT_MX4, 2>(p, s);
     case FMT_A8W8: return stage == 1 ? launch_tile_fs<FMT_A8W8, 1>(p, s) : launch_tile_fs<FMT_A8W8, 2>(p, s);
     default: return hipErrorInvalidValue;
   }

@@ -147,8 +147,9 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
 #pragma unroll
       for (int m = 0; m < NW; ++m) {
         wb[d][cgi][m][0] = ld16_stream(wbase[m] + off);
-        wb[d][cgi][m][1] = ld16_stream(wbase[m] + off + 1024);
-        if constexpr (FMT == FMT_MX) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
+        // MXFP4: one 1 KiB half per tile (lane (g, r): 32 e2m1 values)
+        wb[d][cgi][m][1] = FMT == FMT_MX4 ? make_uint4(0, 0, 0, 0) : ld16_stream(wbase[m] + off + 1024);
+        if constexpr (fmt_mx(FMT)) wsc[d][cgi][m] = sbase[m][scale_tile_off(ev, rb, kt)];
         else wsc[d][cgi][m] = 127;
       }
     }
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
   if constexpr (STAGE == 1) {
     xr = wv_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * esz));
     xoff = xok ? (uint32_t)((size_t)tok_l * p.H * esz) + g * 16 : kWvOutOfRange;
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (fmt_mx(FMT)) {
       xsr = wv_rsrc(p.x_s, (uint32_t)((size_t)p.T * (p.H / 32)));
       xsoff = xok ? (uint32_t)(tok_l * (p.H / 32)) + g : kWvOutOfRange;
     }
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     const size_t rows = (size_t)p.max_blocks * BM;
     xr = wv_rsrc(p.h, (uint32_t)(rows * h_row_bytes<FMT>(p)));
     xoff = xok ? (uint32_t)((size_t)slot_l * h_row_bytes<FMT>(p)) + g * 16 : kWvOutOfRange;
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (fmt_mx(FMT)) {
       xsr = wv_rsrc(p.h_s, (uint32_t)(rows * (p.ld_h / 32)));
       xsoff = xok ? (uint32_t)(slot_l * (p.ld_h / 32)) + g : kWvOutOfRange;
     }
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
     const uint32_t o = xoff + (uint32_t)kt * 128;
     xb[d][0] = wv_load16(xr, o);
     xb[d][1] = wv_load16(xr, o + 64);
-    if constexpr (FMT == FMT_MX)
+    if constexpr (fmt_mx(FMT))
       xsc[d] = (int)__builtin_amdgcn_raw_buffer_load_b8(xsr, (int)(xsoff + (uint32_t)kt * 4), 0, 0);
     else
       xsc[d] = 127;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
 
   if constexpr (STAGE == 1) {
     const size_t slot = (size_t)slot_l;
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (fmt_mx(FMT)) {
       // one MX-32 block per token: the wave's 32 columns
       float v[8], amax = 0.f;
 #pragma unroll
@@ -423,6 +424,7 @@ hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t
       case FMT_F32: return launch_wv<FMT_F32, 1>(p, depth, s);
       case FMT_BF16: return launch_wv<FMT_BF16, 1>(p, depth, s);
       case FMT_MX: return launch_wv<FMT_MX, 1>(p, depth, s);
+      case FMT_MX4: return launch_wv<FMT_MX4, 1>(p, depth, s);
       case FMT_A8W8: return launch_wv<FMT_A8W8, 1>(p, depth, s);
     }
   } else {
@@ -430,6 +432,7 @@ hipError_t launch_gemm_wave(const GemmParams& p, int stage, int fmt, hipStream_t
       case FMT_F32: return launch_wv<FMT_F32, 2>(p, depth, s);
       case FMT_BF16: return launch_wv<FMT_BF16, 2>(p, depth, s);
       case FMT_MX: return launch_wv<FMT_MX, 2>(p, depth, s);
+      case FMT_MX4: return launch_wv<FMT_MX4, 2>(p, depth, s);
       case FMT_A8W8: return launch_wv<FMT_A8W8, 2>(p, depth, s);
     }
   }

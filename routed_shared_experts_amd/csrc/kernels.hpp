@@ -8,7 +8,11 @@
 
 namespace moe {
 
-enum Fmt : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX = 2, FMT_A8W8 = 3 };
+// FMT_MX4: MXFP4 weights (e2m1, e8m0 per 32) with the MX-fp8 activations and
+// intermediate of FMT_MX
+enum Fmt : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX = 2, FMT_A8W8 = 3, FMT_MX4 = 4 };
+// formats whose activations, intermediate and weights carry MX-32 scales
+constexpr bool fmt_mx(int f) { return f == FMT_MX || f == FMT_MX4; }
 
 struct RouteParams {
   const float* logits;

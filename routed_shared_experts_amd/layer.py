@@ -7,7 +7,7 @@ aux-stream mode needs, and calls the library.
 
 import torch
 
-from . import (MoeForwardArgs, MoeWeights, MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_SCALE_NONE,
+from . import (MoeForwardArgs, MoeWeights, MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1, MOE_SCALE_NONE,
                MOE_SCALE_PER_EXPERT, MOE_SCALE_MX32, MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID,
                MOE_LAYOUT_TILED, SHARED_MODES, MOE_OK, MoeError, moe_validate, moe_workspace_bytes,
                moe_forward, moe_pack_weights, moe_pack_mx_scales, moe_status_str, _ptr)
@@ -18,6 +18,7 @@ FORMATS = {
     "bf16": (MOE_BF16, MOE_BF16, MOE_SCALE_NONE, MOE_BF16),
     "mxfp8": (MOE_BF16, MOE_FP8_E4M3, MOE_SCALE_MX32, MOE_BF16),
     "a8w8": (MOE_FP8_E4M3, MOE_FP8_E4M3, MOE_SCALE_PER_EXPERT, MOE_BF16),
+    "mxfp4": (MOE_BF16, MOE_FP4_E2M1, MOE_SCALE_MX32, MOE_BF16),
 }
 
 
@@ -35,7 +36,7 @@ def pack_weights(cfg, inp, stream=None):
     names = ["w13", "w2"] + (["ws13", "ws2"] if cfg.I_s > 0 else [])
     for n in names:
         out[n] = moe_pack_weights(inp[n], stream=stream)
-        if cfg.fmt == "mxfp8":
+        if cfg.fmt in ("mxfp8", "mxfp4"):
             out[n + "_scale"] = moe_pack_mx_scales(inp[n + "_scale"], stream=stream)
     return out
 

@@ -15,19 +15,11 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import TOL, inputs, run_forward, rounding_floor
+from gpu_util import TOL, inputs, run_forward, rounding_floor, auto_block_m, adjacent_codes, compare_mx_h
 
 pytestmark = pytest.mark.gpu
 
 LC = workloads.LayerConfig
-
-
-def _auto_block_m(rows_per_expert):
-    need = 1.5 * rows_per_expert
-    for bm in (16, 32, 64):
-        if need <= bm:
-            return bm
-    return 128
 
 
 def covering_tokens(cfg, ids, n_random, seed):
@@ -39,7 +31,7 @@ def covering_tokens(cfg, ids, n_random, seed):
     for k_total, n_exp, full in ((k, cfg.E, ids),
                                  (k + m, cfg.E + m,
                                   np.concatenate([ids, np.tile(np.arange(cfg.E, cfg.E + m), (T, 1))], 1))):
-        bm = _auto_block_m(T * k_total / n_exp)
+        bm = auto_block_m(T * k_total / n_exp)
         srt = oracle.sort_tokens(full, n_exp, bm)["sorted_pair_ids"]
         P = T * k_total
         part = min(bm, 64)
@@ -106,6 +98,16 @@ def test_mxfp8_every_token(gpu):
     _check_both_modes(cfg, inp, np.arange(cfg.T), lazy=True)
 
 
+def test_mxfp4_decode_every_token(gpu):
+    """The decode batch end to end (the 512-token MXFP4 layer is checked
+    stage by stage in the full-size tests: with 4-bit weights a correct
+    one-code rounding of h near a boundary can move an output by more than
+    a fixed fraction of the RMS)."""
+    cfg = workloads.CONFIGS["mxfp4_decode"]
+    inp = inputs(cfg, gpu)
+    _check_both_modes(cfg, inp, np.arange(cfg.T), lazy=True)
+
+
 def test_a8w8_large_every_block(gpu):
     cfg = workloads.CONFIGS["a8w8_large"]
     inp = inputs(cfg, gpu)
@@ -151,7 +153,7 @@ def _stage1_h(cfg, inp, block_m, dev):
                 group_score_topk=cfg.group_score_topk,
                 score=m.MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else m.MOE_SCORE_SOFTMAX,
                 renormalize=cfg.renormalize, routed_scaling_factor=cfg.routed_scaling_factor)
-    if cfg.fmt == "mxfp8":
+    if cfg.fmt in ("mxfp8", "mxfp4"):
         x = torch.empty((T, H), dtype=torch.uint8, device=dev)
         x_scale = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
         m.moe_quant_mx(W["x"], x, x_scale)
@@ -164,7 +166,7 @@ def _stage1_h(cfg, inp, block_m, dev):
     offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     nblk = torch.empty((4,), dtype=torch.int32, device=dev)
     m.moe_sort_tokens(ids, E, block_m, cap, srt, bexp, counts, offs, nblk)
-    if cfg.fmt == "mxfp8":
+    if cfg.fmt in ("mxfp8", "mxfp4"):
         h = torch.empty((cap, I), dtype=torch.uint8, device=dev)
         hs = torch.empty((cap, I // 32), dtype=torch.uint8, device=dev)
     else:
@@ -179,19 +181,10 @@ def _stage1_h(cfg, inp, block_m, dev):
     a.h, a.h_scale = _ptr(h), _ptr(hs)
     m.moe_stage1(a)
     torch.cuda.synchronize()
-    if cfg.fmt == "mxfp8":
+    if cfg.fmt in ("mxfp8", "mxfp4"):
         return srt.cpu().numpy(), h.cpu().numpy(), hs.cpu().numpy()
     bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
     return srt.cpu().numpy(), bits, (hs.cpu().numpy() if hs is not None else None)
-
-
-def _adjacent(a, b, sign_bit, mag_mask):
-    """Codes one step apart (or equal) in a sign-magnitude format whose
-    magnitudes are ordered like the codes (bf16 and e4m3fn both are)."""
-    a, b = a.astype(np.int64), b.astype(np.int64)
-    sa, sb = a & sign_bit, b & sign_bit
-    ma, mb = a & mag_mask, b & mag_mask
-    return np.where(sa == sb, np.abs(ma - mb) <= 1, (ma + mb) <= 1)
 
 
 STAGE1_CASES = {
@@ -201,6 +194,8 @@ STAGE1_CASES = {
                 fmt="mxfp8", gated=False, bias_std=0.1),
     "a8w8": LC("s1_a8w8", T=120, H=512, E=16, I=256, I_s=0, topk=4, score="sigmoid", n_group=4, topk_group=2,
                fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    "mxfp4": LC("s1_mxfp4", T=120, H=512, E=16, I=256, I_s=0, topk=4, score="sigmoid", n_group=4, topk_group=2,
+                fmt="mxfp4", gated=False, bias_std=0.1),
 }
 
 
@@ -218,6 +213,8 @@ def test_stage1_intermediate_matches_oracle(gpu, name, block_m):
     across a power of two changes its scale by one, which requantises the
     block: those blocks are counted, not compared code by code."""
     cfg = STAGE1_CASES[name]
+    if cfg.fmt == "mxfp4" and block_m == 256:
+        pytest.skip("256-row blocks: the LDS-staged kernels take no e2m1 weights")
     inp = inputs(cfg, gpu)
     srt, got, got_s = _stage1_h(cfg, inp, block_m, gpu)
     host = workloads.to_host(inp)
@@ -237,33 +234,19 @@ def test_stage1_intermediate_matches_oracle(gpu, name, block_m):
             diff = g != ref_bits
             gv, rv = oracle.bf16_bits_to_f64(g), oracle.bf16_bits_to_f64(ref_bits)
             row_max = np.abs(rv).max(axis=1, keepdims=True)
-            ok = _adjacent(g, ref_bits, 0x8000, 0x7FFF) | (np.abs(gv - rv) <= 2.0 ** -12 * row_max)
+            ok = adjacent_codes(g, ref_bits, 0x8000, 0x7FFF) | (np.abs(gv - rv) <= 2.0 ** -12 * row_max)
             assert ok[diff].all(), name
             n_val += diff.size
             n_flip += int(diff.sum())
             if cfg.fmt == "a8w8":
                 amax = np.abs(oracle.bf16_bits_to_f64(g)).max(axis=1).astype(np.float32)
                 assert np.array_equal(got_s[slots], amax), "row maxima differ from the rows' own values"
-        else:
-            rs, rq = oracle.mx_quantize(oracle.bf16_bits_to_f64(ref_bits).astype(np.float32))
-            gs, gq = got_s[slots], got[slots]
-            same = gs == rs
-            assert (np.abs(gs.astype(int) - rs.astype(int)) <= 1).all(), "an MX block scale moved by more than one"
-            n_blk += same.size
-            n_blk_flip += int((~same).sum())
-            cmp = np.repeat(same, 32, axis=1)
-            diff = (gq != rq) & cmp
-            # one code apart, or (small values) within 2^-12 of the block's
-            # largest magnitude, where the fp32 accumulation error lives
-            gv, rv = oracle.mx_dequantize(gs, gq), oracle.mx_dequantize(rs, rq)
-            blk_max = np.repeat(np.abs(rv).reshape(rv.shape[0], -1, 32).max(axis=2), 32, axis=1)
-            ok = _adjacent(gq, rq, 0x80, 0x7F) | (np.abs(gv - rv) <= 2.0 ** -12 * blk_max)
-            assert ok[diff].all(), name
-            n_val += int(cmp.sum())
-            n_flip += int(diff.sum())
+        else:  # mxfp8, mxfp4: MX-32 e4m3 intermediate
+            nv, nf, nb, nbf = compare_mx_h(got[slots], got_s[slots], inter["h"], name)
+            n_val, n_flip, n_blk, n_blk_flip = n_val + nv, n_flip + nf, n_blk + nb, n_blk_flip + nbf
     rate = n_flip / max(n_val, 1)
     msg = f"stage 1 {name}/bm{block_m}: {n_flip} of {n_val} values one code from the oracle's (rate {rate:.2e})"
-    if cfg.fmt == "mxfp8":
+    if cfg.fmt in ("mxfp8", "mxfp4"):
         msg += f"; {n_blk_flip} of {n_blk} MX blocks with a scale one step off"
         assert n_blk_flip <= 0.01 * n_blk
     print(msg)
@@ -271,7 +254,7 @@ def test_stage1_intermediate_matches_oracle(gpu, name, block_m):
     # relative to the sum of their magnitudes (measured on MI355X: at most
     # 2^-15.2, mean 1.3e-6), far coarser than fp32 addition; a8w8's unit-scale
     # codes put many h values that close to a bf16 rounding boundary
-    assert rate <= {"bf16": 1e-3, "mxfp8": 1e-2, "a8w8": 5e-2}[cfg.fmt]
+    assert rate <= {"bf16": 1e-3, "mxfp8": 1e-2, "mxfp4": 1e-2, "a8w8": 5e-2}[cfg.fmt]
 
 
 # ---- non-finite values in the stage-2 reduction ------------------------------

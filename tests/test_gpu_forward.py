@@ -24,6 +24,9 @@ SMALL = {
                       topk_group=2, routed_scaling_factor=2.5, fmt="mxfp8", gated=False, bias_std=0.1),
     "small_a8w8": LC("small_a8w8", T=90, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                      topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    # MXFP4 weights, MX-fp8 activations; I_s = 512 over I = 256: two pseudo chunks
+    "small_mxfp4": LC("small_mxfp4", T=70, H=512, E=16, I=256, I_s=512, topk=4, score="sigmoid", n_group=4,
+                      topk_group=2, routed_scaling_factor=2.5, fmt="mxfp4", gated=False, bias_std=0.1),
     # H = 2112: 33 stage-2 column tiles, several tile groups per XCD queue, so
     # the bf16 reduction counts arrivals per (token, tile) instead of per group
     "wide_bf16": LC("wide_bf16", T=150, H=2112, E=8, I=128, I_s=128, topk=2, fmt="bf16", logits="zipf",
@@ -40,8 +43,8 @@ def test_small_layers_all_outputs(gpu, name, mode, block_m):
     bf16 / MX / a8w8 and the LDS-staged fallback for f32 (up to 128); 0 is the
     automatic choice."""
     cfg = SMALL[name]
-    if cfg.fmt == "f32" and block_m == 256:
-        pytest.skip("256-row blocks are provided by the tiled kernels only (not f32)")
+    if cfg.fmt in ("f32", "mxfp4") and block_m == 256:
+        pytest.skip("256-row blocks: the LDS-staged kernels, which take neither f32 nor e2m1 weights")
     if mode == "pseudo" and cfg.fmt == "a8w8" and cfg.I_s > cfg.I:
         pytest.skip("per-row fp8 intermediate needs a single pseudo chunk")
     inp = inputs(cfg, gpu)
