@@ -24,6 +24,9 @@ SMALL = {
                       topk_group=2, routed_scaling_factor=2.5, fmt="mxfp8", gated=False, bias_std=0.1),
     "small_a8w8": LC("small_a8w8", T=90, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                      topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    # softmax scores with grouped top-k (routing in its own launch)
+    "small_softmax_groups": LC("small_softmax_groups", T=80, H=256, E=32, I=128, I_s=128, topk=6,
+                               score="softmax", n_group=8, topk_group=3, fmt="bf16"),
     # MXFP4 weights, MX-fp8 activations; I_s = 512 over I = 256: two pseudo chunks
     "small_mxfp4": LC("small_mxfp4", T=70, H=512, E=16, I=256, I_s=512, topk=4, score="sigmoid", n_group=4,
                       topk_group=2, routed_scaling_factor=2.5, fmt="mxfp4", gated=False, bias_std=0.1),

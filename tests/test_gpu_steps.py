@@ -110,6 +110,24 @@ def test_route_grouped_with_ties_and_k_equals_e(gpu):
     assert np.array_equal(ids, rid) and np.abs(w - rw).max() <= 1e-6
 
 
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_route_softmax_with_groups(gpu, renormalize):
+    """Softmax scores with grouped top-k (group score: the largest one or the
+    sum of the two largest logits of the group), several group sizes,
+    against the oracle bit-exact."""
+    rng = np.random.default_rng(14)
+    lg = rng.normal(0, 1.5, (300, 64)).astype(np.float32)
+    lg[::5] = np.round(lg[::5])  # tie-heavy rows
+    lg_t = torch.from_numpy(lg).to(gpu)
+    for ng, gk, gtop in [(8, 3, 2), (8, 4, 1), (4, 2, 2), (16, 5, 2)]:
+        ids, w = _route_gpu(lg_t, 6, score="softmax", n_group=ng, topk_group=gk, group_score_topk=gtop,
+                            renormalize=renormalize, routed_scaling_factor=1.75)
+        rid, rw = oracle.route(lg, topk=6, score="softmax", n_group=ng, topk_group=gk, group_score_topk=gtop,
+                               renormalize=renormalize, routed_scaling_factor=1.75)
+        assert np.array_equal(ids, rid), (ng, gk, gtop)
+        assert np.abs(w - rw).max() <= 2e-6
+
+
 @pytest.mark.parametrize("E", [320, 512])
 def test_route_at_the_expert_and_slot_limits(gpu, E):
     """E up to 512 routed experts (eight per lane) and k + pseudo slots up to
