@@ -101,6 +101,12 @@ typedef enum {
 
 typedef enum { MOE_STAGE2_STORE = 0, MOE_STAGE2_ACCUMULATE = 1 } moe_stage2_mode;
 
+/* Gated activation of stage 1, h = act(a_gate) * a_up (AITER PR 6106,
+ * "Technical Details": the activation follows the scales and the bias on the
+ * fp32 accumulator).  SILU: g * sigmoid(g).  GELU_TANH: the tanh form of
+ * GELU, g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))). */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_TANH = 1 } moe_activation;
+
 typedef enum {
   MOE_FEATURE_ACCUMULATE_OUTPUT = 1, /* stage 2 accumulates onto an addend */
   MOE_FEATURE_PSEUDO_SHARED = 2,     /* heterogeneous shared pseudo-experts */
@@ -109,7 +115,9 @@ typedef enum {
   MOE_FEATURE_A8W8 = 5,
   MOE_FEATURE_F32 = 6,
   MOE_FEATURE_BF16 = 7,
-  MOE_FEATURE_MXFP4 = 8
+  MOE_FEATURE_MXFP4 = 8,
+  MOE_FEATURE_EXPERT_BIAS = 9, /* per-expert bias on the stage-1 and stage-2 accumulators */
+  MOE_FEATURE_GELU_TANH = 10   /* MOE_ACT_GELU_TANH */
 } moe_feature;
 
 /* Weight layout.  Logically every weight matrix is row-major: rows = output
@@ -141,6 +149,13 @@ typedef struct {
   int32_t dtype;         /* moe_dtype */
   int32_t scale;         /* moe_scale: NONE, PER_EXPERT or MX32 */
   int32_t layout;        /* moe_layout of w13, w2 and MX32 scales: must be MOE_LAYOUT_TILED */
+  /* optional per-expert biases, fp32, each NULL for none (AITER PR 6106,
+   * "Technical Details": added to the fp32 accumulator after the scales and
+   * before the activation): b13 [n][2*width] (gate entries, then up entries)
+   * on stage 1's a = x . W13^T; b2 [n][H] on stage 2's o = h . W2^T, before
+   * the routing weight or the shared gate multiplies o */
+  const float* b13;
+  const float* b2;
 } moe_weights;
 
 /* Everything one layer forward needs. */
@@ -174,6 +189,7 @@ typedef struct {
    * kernel and [5]/[6] those of the routed stage-2 GEMM kernel (stamped by
    * the kernels' own dispatch) */
   hipEvent_t* timing_events;
+  int32_t activation; /* moe_activation of routed and shared experts (0 = SILU) */
 } moe_forward_args;
 
 /* Pure host check of a forward request; makes no HIP call.  Returns MOE_OK,
@@ -326,7 +342,8 @@ moe_status moe_sort_tokens(const int32_t* topk_ids, int32_t T, int32_t k_total,
  * E <= e < E + n_pseudo is shared pseudo-expert p = e - E: rows
  * [p*I, min((p+1)*I, I_s)) of the shared gate and up halves and the same
  * columns of the shared W2 (exact by linearity of the down projection and the
- * elementwise SiLU-mul).  dense = 1 instead runs the whole shared expert
+ * elementwise activation-mul), with the same entries of the shared b13; the
+ * shared b2 belongs to pseudo-expert 0 alone.  dense = 1 instead runs the whole shared expert
  * (width I_s) over tokens 0..T-1 with no sorted problem. */
 typedef struct {
   int32_t T, H, E, I, I_s, n_pseudo, k_total;
@@ -368,6 +385,7 @@ typedef struct {
                           then the work-queue state of the stage-2 kernels */
   int32_t expected_arrivals; /* contributions per token: must equal k_total */
   hipEvent_t addend_ready;   /* waited on (device-side) before stage 2, or NULL */
+  int32_t activation;        /* moe_activation (stage 1) */
 } moe_stage_args;
 
 /* Number of int32 counters moe_stage2_accum (ACCUMULATE) needs, all zero on

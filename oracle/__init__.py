@@ -68,6 +68,7 @@ from .layer import (
     expert_weights,
     shared_weights,
     expert_mlp,
+    activation,
     moe_layer,
     stage1_reference,
 )
@@ -77,6 +78,6 @@ __all__ = [
     "e8m0_decode", "mx_quantize", "mx_dequantize", "row_quantize_e4m3", "e2m1_decode", "e2m1_unpack",
     "mx4_dequantize",
     "spec_exp", "spec_sigmoid", "route", "sort_tokens", "gate",
-    "decode_activations", "expert_weights", "shared_weights", "expert_mlp",
+    "decode_activations", "expert_weights", "shared_weights", "expert_mlp", "activation",
     "moe_layer", "stage1_reference",
 ]

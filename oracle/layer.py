@@ -7,7 +7,9 @@ output, with the routed scaling folded into the top-k weights):
 
     y_t = sum_j w_tj * E_{e_tj}(x_t) + gamma_t * S(x_t)
 
-    E(x) = W2 . Q_h( SiLU(x . Wg^T) * (x . Wu^T) )   (SwiGLU expert)
+    E(x) = W2 . Q_h( act(x . Wg^T + bg) * (x . Wu^T + bu) ) + b2
+                                                      (gated expert; act = SiLU
+                                                       by default)
     gamma_t = sigmoid(x_t . g)                        (vLLM PR 56789, Summary:
                                                        the shared-expert gate is
                                                        sigmoid of a Linear(H, 1))
@@ -28,6 +30,16 @@ activation and the fused quantisation; MX GEMMs use 32-element K blocks):
                quantised per row to e4m3 with an fp32 row scale.
 * fmt 'mxfp4': as 'mxfp8' (x and h MX-32 e4m3) with MXFP4 weights: e2m1
                elements, an e8m0 scale per 32 K elements.
+
+Expert biases and the activation (AITER PR 6106, Technical Details: the
+scales act on the fp32 accumulator before the bias, the activation and the
+fused quantisation): the optional fp32 biases b13 = (bg, bu) [2I] are added to
+the scaled stage-1 accumulator, b2 [H] to the scaled stage-2 output of the
+expert, before its routing weight (or the shared gate) multiplies it -- the
+reading of a bias as part of each projection.  act is SiLU, g * sigmoid(g),
+or the tanh form of GELU, g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))
+(the pages name no particular alternative; GELU-gated experts are the common
+one).
 
 Every dot product is float64 over the exactly decoded operands, so the only
 roundings are the quantisation points themselves.  The shared expert is
@@ -127,17 +139,44 @@ def quantize_h(h, fmt):
     raise ValueError(fmt)
 
 
-def expert_mlp(xr, sx, W13, W2, s13, s2, fmt, intermediates=False):
-    """One SwiGLU expert on rows xr [n, H] with per-row input scale sx [n]."""
+def activation(g, act):
+    """The gate activation in float64: 'silu' g / (1 + e^-g); 'gelu_tanh'
+    g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))."""
+    if act == "silu":
+        return g / (1.0 + np.exp(-g))
+    if act == "gelu_tanh":
+        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+    raise ValueError(act)
+
+
+def _f64(v):
+    return None if v is None else np.asarray(v, dtype=np.float32).astype(np.float64)
+
+
+def expert_mlp(xr, sx, W13, W2, s13, s2, fmt, intermediates=False, b13=None, b2=None, act="silu"):
+    """One gated expert on rows xr [n, H] with per-row input scale sx [n]
+    (optional fp32 biases b13 [2I], b2 [H]; act 'silu' or 'gelu_tanh')."""
     I = W2.shape[1]
     a = (xr @ W13.T) * sx[:, None] * s13
+    if b13 is not None:
+        a = a + _f64(b13)[None, :]
     g, u = a[:, :I], a[:, I:]
-    h = g / (1.0 + np.exp(-g)) * u
+    h = activation(g, act) * u
     ht, sh = quantize_h(h, fmt)
     o = (ht @ W2.T) * sh[:, None] * s2
+    if b2 is not None:
+        o = o + _f64(b2)[None, :]
     if intermediates:
         return o, {"a": a, "h": h, "h_tilde": ht, "h_scale": sh}
     return o
+
+
+def _expert_bias(inp, e):
+    """(b13, b2) of routed expert e, or of the shared expert for e = None."""
+    if e is None:
+        return inp.get("bs13"), inp.get("bs2")
+    b13, b2 = inp.get("b13"), inp.get("b2")
+    return (None if b13 is None else b13[e]), (None if b2 is None else b2[e])
 
 
 def route_layer(inp, prm, gamma=None, n_pseudo=0):
@@ -169,15 +208,18 @@ def moe_layer(inp, prm, tokens=None):
     y = np.zeros((tokens.size, prm.H))
     sel_ids = ids[tokens]
     sel_w = w[tokens]
+    act = getattr(prm, "activation", "silu")
     for e in np.unique(sel_ids):
         rows, slots = np.nonzero(sel_ids == e)
         W13, W2, s13, s2 = expert_weights(inp, fmt, int(e))
+        b13, b2 = _expert_bias(inp, int(e))
         t = tokens[rows]
-        o = expert_mlp(xh[t], sx[t], W13, W2, s13, s2, fmt)
+        o = expert_mlp(xh[t], sx[t], W13, W2, s13, s2, fmt, b13=b13, b2=b2, act=act)
         np.add.at(y, rows, sel_w[rows, slots][:, None] * o)
     if prm.I_s > 0:
         Ws13, Ws2, s13, s2 = shared_weights(inp, fmt)
-        o = expert_mlp(xh[tokens], sx[tokens], Ws13, Ws2, s13, s2, fmt)
+        b13, b2 = _expert_bias(inp, None)
+        o = expert_mlp(xh[tokens], sx[tokens], Ws13, Ws2, s13, s2, fmt, b13=b13, b2=b2, act=act)
         y += gamma[tokens][:, None] * o
     return {"y": y, "ids": ids, "w": w, "gamma": gamma, "tokens": tokens}
 
@@ -189,7 +231,10 @@ def stage1_reference(inp, prm, e, token_rows):
     xh, sx = decode_activations(inp, fmt)
     if e == prm.E:
         W13, W2, s13, s2 = shared_weights(inp, fmt)
+        b13, b2 = _expert_bias(inp, None)
     else:
         W13, W2, s13, s2 = expert_weights(inp, fmt, e)
-    _, inter = expert_mlp(xh[token_rows], sx[token_rows], W13, W2, s13, s2, fmt, intermediates=True)
+        b13, b2 = _expert_bias(inp, e)
+    _, inter = expert_mlp(xh[token_rows], sx[token_rows], W13, W2, s13, s2, fmt, intermediates=True,
+                          b13=b13, b2=b2, act=getattr(prm, "activation", "silu"))
     return inter

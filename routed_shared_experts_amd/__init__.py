@@ -28,8 +28,11 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_SHARED_NONE, MOE_SHARED_PSEUDO, MOE_SHARED_AUX, MOE_SHARED_AUTO = 0, 1, 2, 3
 MOE_STAGE2_STORE, MOE_STAGE2_ACCUMULATE = 0, 1
 MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_TILED = 0, 1
+MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 (MOE_FEATURE_ACCUMULATE_OUTPUT, MOE_FEATURE_PSEUDO_SHARED, MOE_FEATURE_AUX_STREAM,
- MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16, MOE_FEATURE_MXFP4) = 1, 2, 3, 4, 5, 6, 7, 8
+ MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16, MOE_FEATURE_MXFP4,
+ MOE_FEATURE_EXPERT_BIAS, MOE_FEATURE_GELU_TANH) = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+ACTIVATIONS = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 
 SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE_SHARED_AUX,
                 "auto": MOE_SHARED_AUTO}
@@ -45,7 +48,8 @@ c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w13", c_void_p), ("w2", c_void_p), ("w13_scale", c_void_p), ("w2_scale", c_void_p),
-                ("dtype", c_int32), ("scale", c_int32), ("layout", c_int32)]
+                ("dtype", c_int32), ("scale", c_int32), ("layout", c_int32), ("b13", c_void_p),
+                ("b2", c_void_p)]
 
 
 class MoeForwardArgs(ctypes.Structure):
@@ -56,7 +60,7 @@ class MoeForwardArgs(ctypes.Structure):
                 ("x", c_void_p), ("x_dtype", c_int32), ("x_row_scale", c_void_p),
                 ("routed", MoeWeights), ("shared", MoeWeights), ("gate_w", c_void_p),
                 ("shared_mode", c_int32), ("block_m", c_int32), ("out", c_void_p),
-                ("out_dtype", c_int32), ("timing_events", c_void_p)]
+                ("out_dtype", c_int32), ("timing_events", c_void_p), ("activation", c_int32)]
 
 
 class MoeStageArgs(ctypes.Structure):
@@ -67,7 +71,8 @@ class MoeStageArgs(ctypes.Structure):
                 ("block_expert", c_void_p), ("num_blocks", c_void_p), ("h", c_void_p),
                 ("h_scale", c_void_p), ("pair_w", c_void_p), ("gamma", c_void_p), ("acc", c_void_p),
                 ("pair_out", c_void_p), ("out", c_void_p), ("out_dtype", c_int32), ("mode", c_int32),
-                ("counters", c_void_p), ("expected_arrivals", c_int32), ("addend_ready", c_void_p)]
+                ("counters", c_void_p), ("expected_arrivals", c_int32), ("addend_ready", c_void_p),
+                ("activation", c_int32)]
 
 
 class MoeError(RuntimeError):

@@ -43,8 +43,11 @@ bool weights_ok(const moe_weights& w, int fmt) {
     if (fmt_mx(fmt) && (((uintptr_t)w.w13_scale & 3u) || ((uintptr_t)w.w2_scale & 3u))) return false;
     if (fmt == FMT_A8W8 && (((uintptr_t)w.w13_scale & 3u) || ((uintptr_t)w.w2_scale & 3u))) return false;
   }
+  if (((uintptr_t)w.b13 & 3u) || ((uintptr_t)w.b2 & 3u)) return false;  // fp32 biases
   return true;
 }
+
+bool activation_ok(int32_t act) { return act == MOE_ACT_SILU || act == MOE_ACT_GELU_TANH; }
 
 // MOE_OK, or the error for a weight family in a layout the kernels do not read
 moe_status layout_status(const moe_weights& w) {
@@ -122,6 +125,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (a->bias && ((uintptr_t)a->bias & 3u)) return MOE_ERR_INVALID_ARG;
   if (a->bias && a->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (a->out_dtype != MOE_F32 && a->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!activation_ok(a->activation)) return MOE_ERR_INVALID_ARG;
   if (a->shared_mode < MOE_SHARED_NONE || a->shared_mode > MOE_SHARED_AUTO) return MOE_ERR_INVALID_ARG;
   if (a->block_m != 0 && a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128 &&
       a->block_m != 256)
@@ -261,6 +265,10 @@ void fill_weights(GemmParams& g, const moe_weights& r, const moe_weights& s) {
   g.ws2 = static_cast<const uint8_t*>(s.w2);
   g.ws13_s = s.w13_scale;
   g.ws2_s = s.w2_scale;
+  g.b13 = r.b13;
+  g.b2 = r.b2;
+  g.bs13 = s.b13;
+  g.bs2 = s.b2;
 }
 
 thread_local hipError_t g_last_hip = hipSuccess;  // last HIP failure reported as MOE_ERR_HIP
@@ -346,7 +354,9 @@ int32_t moe_query_feature(int32_t feature) {
     case MOE_FEATURE_MXFP4:
     case MOE_FEATURE_A8W8:
     case MOE_FEATURE_F32:
-    case MOE_FEATURE_BF16: return 1;
+    case MOE_FEATURE_BF16:
+    case MOE_FEATURE_EXPERT_BIAS:
+    case MOE_FEATURE_GELU_TANH: return 1;
     default: return 0;
   }
 }
@@ -499,6 +509,7 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   if (a->block_m != 16 && a->block_m != 32 && a->block_m != 64 && a->block_m != 128 && a->block_m != 256)
     return MOE_ERR_INVALID_ARG;
   if (a->max_blocks <= 0) return MOE_ERR_INVALID_ARG;
+  if (!activation_ok(a->activation)) return MOE_ERR_INVALID_ARG;
   const moe_weights& wf = a->dense ? a->shared : a->routed;
   fmt = weights_fmt(wf);
   if (fmt < 0) return MOE_ERR_UNSUPPORTED;
@@ -526,6 +537,7 @@ static moe_status stage_params(const moe_stage_args* a, GemmParams& g, int& fmt)
   g.n_pseudo = a->n_pseudo;
   g.k_total = a->k_total;
   fill_weights(g, a->routed, a->shared);
+  g.act = a->activation;
   g.x = static_cast<const uint8_t*>(a->x);
   g.x_s = a->x_scale;
   g.dense = a->dense != 0;
@@ -683,6 +695,7 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   g.n_pseudo = pl.m;
   g.k_total = pl.k_total;
   fill_weights(g, a->routed, a->shared);
+  g.act = a->activation;
   const void* x_stage = fmt_mx(fmt) ? static_cast<const void*>(xq) : a->x;
   const void* xs_stage = fmt_mx(fmt) ? static_cast<const void*>(xs)
                                        : (fmt == FMT_A8W8 ? static_cast<const void*>(a->x_row_scale) : nullptr);

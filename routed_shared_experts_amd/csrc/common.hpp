@@ -85,6 +85,33 @@ __device__ __forceinline__ float spec_sigmoid(float x) {
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
+// act(g) * u: act = 0 SiLU; act = 1 GELU in its tanh form, written through
+// 1 + tanh(z) = 2 sigmoid(2 z): g * sigmoid(2 sqrt(2/pi) (g + 0.044715 g^3)).
+__device__ __forceinline__ float act_mul(float g, float u, int act) {
+  if (act == 1) {
+    const float z = g * (1.5957691216057308f + 0.07135481627159537f * (g * g));
+    return g / (1.0f + __expf(-z)) * u;
+  }
+  return silu_mul(g, u);
+}
+// Bias entry i; without a bias (or past the valid width) -0, which adds to
+// any value, signed zeros included, without changing it.
+__device__ __forceinline__ float bias_at(const float* b, int i, int width = 0x7FFFFFFF) {
+  return (b && i < width) ? b[i] : -0.0f;
+}
+// The epilogue of the register-heavy kernels, specialised: EPI = false is
+// the plain SiLU-mul with no bias (the common case, no extra registers);
+// EPI = true reads the biases and the activation choice.
+template <bool EPI>
+__device__ __forceinline__ float epi_bias(const float* b, int i, int width = 0x7FFFFFFF) {
+  if constexpr (EPI) return bias_at(b, i, width);
+  else return -0.0f;
+}
+template <bool EPI>
+__device__ __forceinline__ float epi_act(float g, float u, int act) {
+  if constexpr (EPI) return act_mul(g, u, act);
+  else return silu_mul(g, u);
+}
 
 // ---- wave64 reductions --------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

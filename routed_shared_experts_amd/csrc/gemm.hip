@@ -5,7 +5,7 @@
 // fp32 accumulation; the per-token and per-expert scales multiply the fp32
 // accumulator before the activation (AITER PR 6106, "Technical Details"),
 // MX-32 block scales are applied by the block-scaled MFMA inside the K loop;
-// the epilogue computes h = SiLU(a_gate) * a_up and rounds / quantises it to
+// the epilogue computes h = act(a_gate) * a_up (bias added first) and rounds / quantises it to
 // the stage-2 input format (bf16, MX-32 e4m3, or bf16 plus a per-row amax
 // from which stage 2 derives the per-row e4m3 scale).
 //
@@ -274,9 +274,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         float val;
         if constexpr (STAGE == 1) {
           const float sc = s_rs[r] * ev.wscale;
-          val = silu_mul(acc[i][j][v] * sc, acc2[i][j][v] * sc);
+          val = act_mul(acc[i][j][v] * sc + bias_at(ev.bg, n0 + c, ev.width),
+                        acc2[i][j][v] * sc + bias_at(ev.bu, n0 + c, ev.width), p.act);
         } else {
-          val = acc[i][j][v] * (s_rs[r] * ev.wscale);
+          val = acc[i][j][v] * (s_rs[r] * ev.wscale) + bias_at(ev.b2, n0 + c);
         }
         sT[r * LDT + c] = val;
       }

@@ -88,6 +88,9 @@ struct ExpertView {
   int width;           // stage 1: valid h columns; stage 2: valid K (h columns)
   int tb;              // bytes of one weight tile
   float wscale;        // A8W8 per-expert scale
+  const float* bg;     // stage 1: bias of the view's gate column 0 (or NULL)
+  const float* bu;     // stage 1: bias of the view's up column 0 (or NULL)
+  const float* b2;     // stage 2: bias of output column 0 (or NULL; pseudo-expert 0 only)
 };
 
 // Byte offset of tile (row block rb, K tile kt) of a view, and of its scales.
@@ -111,6 +114,10 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
       v.wb = v.wa + wbytes<FMT>(I, H);
       v.nkt = H * esz / 128;
       v.width = I;
+      if (p.b13) {
+        v.bg = p.b13 + (size_t)e * 2 * I;
+        v.bu = v.bg + I;
+      }
       if (fmt_mx(FMT)) {
         v.sa = static_cast<const uint8_t*>(p.w13_s) + (size_t)e * 2 * I * (H / 32);
         v.sb = v.sa + (size_t)I * (H / 32);
@@ -120,6 +127,7 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
       v.wa = p.w2 + wbytes<FMT>((size_t)e * H, I);
       v.nkt = I * esz / 128;
       v.width = I;
+      if (p.b2) v.b2 = p.b2 + (size_t)e * H;
       if (fmt_mx(FMT)) v.sa = static_cast<const uint8_t*>(p.w2_s) + (size_t)e * H * (I / 32);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.w2_s)[e];
     }
@@ -134,6 +142,10 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
       v.wb = p.ws13 + wbytes<FMT>(Is + col0, H);
       v.nkt = H * esz / 128;
       v.width = w;
+      if (p.bs13) {
+        v.bg = p.bs13 + col0;
+        v.bu = p.bs13 + Is + col0;
+      }
       if (fmt_mx(FMT)) {
         v.sa = static_cast<const uint8_t*>(p.ws13_s) + (size_t)col0 * (H / 32);
         v.sb = static_cast<const uint8_t*>(p.ws13_s) + (size_t)(Is + col0) * (H / 32);
@@ -145,6 +157,7 @@ __device__ __forceinline__ ExpertView resolve_expert(const GemmParams& p, int e)
       v.nkt = Is * esz / 128;
       v.kt0 = col0 * esz / 128;
       v.width = w;
+      if (c == 0) v.b2 = p.bs2;
       if (fmt_mx(FMT)) v.sa = static_cast<const uint8_t*>(p.ws2_s);
       if (FMT == FMT_A8W8) v.wscale = static_cast<const float*>(p.ws2_s)[0];
     }

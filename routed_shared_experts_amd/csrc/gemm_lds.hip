@@ -3,7 +3,7 @@
 //
 // What it computes is what gemm_tile.hip computes (stage 1: x_gathered .
 // W13[e]^T, the per-token / per-expert scales on the fp32 accumulator, MX-32
-// block scales inside the block-scaled MFMA, SiLU(gate) * up rounded or
+// block scales inside the block-scaled MFMA, bias, act(gate) * up rounded or
 // quantised to the stage-2 format -- AITER PR 6106, "Technical Details";
 // stage 2: h . W2[e]^T, the weighted pair rows and the last-arrival reduction
 // onto the shared-expert addend -- vLLM PR 65207, "Purpose", commit 2); the
@@ -86,7 +86,7 @@ __device__ __forceinline__ void mfma_frag(f32x4& acc, const uint4& a0, const uin
 // c0 .. c0 + 127 of expert view ev; stage 2: reduction tiles tiles[0..3]
 // (tile < 0: none).  Fills the row tables first; the caller synchronises
 // before the shared memory is reused.
-template <int FMT, int STAGE>
+template <int FMT, int STAGE, bool EPI>
 __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int b, const ExpertView& ev, int c0,
                                           const int (&tiles)[4]) {
   constexpr int esz = FmtInfo<FMT>::esz;
@@ -321,8 +321,12 @@ __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int 
           for (int jj = 0; jj < 4; ++jj) {
             uint32_t bits[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              bits[v] = f32_to_bf16(silu_mul(acc32[i][n][4 * jj + v] * sc, acc32[i + 2][n][4 * jj + v] * sc));
+            for (int v = 0; v < 4; ++v) {
+              const int col = hc0 + 4 * (lane / 32) + 32 * i + 8 * jj + v;
+              bits[v] = f32_to_bf16(epi_act<EPI>(acc32[i][n][4 * jj + v] * sc + epi_bias<EPI>(ev.bg, col, ev.width),
+                                            acc32[i + 2][n][4 * jj + v] * sc + epi_bias<EPI>(ev.bu, col, ev.width),
+                                            p.act));
+            }
             *reinterpret_cast<uint2*>(dst + 32 * i + 8 * jj) =
                 make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
           }
@@ -342,7 +346,11 @@ __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) hv[j][v] = silu_mul(acc[j][q][v] * sc, acc[j + 4][q][v] * sc);
+          for (int v = 0; v < 4; ++v) {
+            const int col = hc0 + 16 * j + 4 * g + v;
+            hv[j][v] = epi_act<EPI>(acc[j][q][v] * sc + epi_bias<EPI>(ev.bg, col, ev.width),
+                               acc[j + 4][q][v] * sc + epi_bias<EPI>(ev.bu, col, ev.width), p.act);
+          }
         if constexpr (mx) {
           // columns hc0 + 32 k .. + 31 (j = 2 k, 2 k + 1) are one MX-32 block
 #pragma unroll
@@ -437,7 +445,8 @@ __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int 
           for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              acc32[2 * u + ii][n][v] = wgt * (acc32[2 * u + ii][n][v] * sc);
+              acc32[2 * u + ii][n][v] =
+                  wgt * (acc32[2 * u + ii][n][v] * sc + epi_bias<EPI>(ev.b2, 64 * t + 32 * ii + 8 * (v / 4) + 4 * hh + v % 4));
               amax = tile_amax(amax, acc32[2 * u + ii][n][v]);
             }
           amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
@@ -468,7 +477,7 @@ __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int 
           for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              acc[4 * u + jj][q][v] = wgt * (acc[4 * u + jj][q][v] * sc);
+              acc[4 * u + jj][q][v] = wgt * (acc[4 * u + jj][q][v] * sc + epi_bias<EPI>(ev.b2, 64 * t + 16 * jj + 4 * g + v));
               amax = tile_amax(amax, acc[4 * u + jj][q][v]);
             }
           amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
@@ -526,7 +535,7 @@ __device__ __forceinline__ void lds_block(const GemmParams& p, LdsSmem& sm, int 
 
 // Stage 1: one workgroup per (256-row block, 128 h columns), expert-major
 // and XCD-contiguous like the tiled kernels.
-template <int FMT>
+template <int FMT, bool EPI>
 __global__ __launch_bounds__(kLdsThreads) void gemm_lds_stage1_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) LdsSmem sm;
   const int n_col = p.I / 128;
@@ -540,12 +549,12 @@ __global__ __launch_bounds__(kLdsThreads) void gemm_lds_stage1_kernel(GemmParams
   const int c0 = nc * 128;
   if (c0 >= ev.width) return;  // past a narrow pseudo-expert chunk (uniform)
   const int none[4] = {-1, -1, -1, -1};
-  lds_block<FMT, 1>(p, sm, b, ev, c0, none);
+  lds_block<FMT, 1, EPI>(p, sm, b, ev, c0, none);
 }
 
 // Stage 2 ACCUMULATE: persistent workgroups draining the per-XCD queues
 // (queue x: items (block, group j), tiles t = x + 8 (4 j + u), u = 0..3).
-template <int FMT>
+template <int FMT, bool EPI>
 __global__ __launch_bounds__(kLdsThreads) void gemm_lds_accum_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) LdsSmem sm;
   const int tid = threadIdx.x;
@@ -583,7 +592,7 @@ __global__ __launch_bounds__(kLdsThreads) void gemm_lds_accum_kernel(GemmParams 
         tiles[u] = t < n64 ? t : -1;
       }
       const ExpertView ev = resolve_expert<FMT, 2>(p, e);
-      lds_block<FMT, 2>(p, sm, b, ev, 0, tiles);
+      lds_block<FMT, 2, EPI>(p, sm, b, ev, 0, tiles);
       __syncthreads();  // the next item rewrites the row tables and buffers
     }
   }
@@ -605,11 +614,11 @@ bool lds_kernel_fits(const GemmParams& p, int stage, int fmt) {
   return (size_t)p.max_blocks * kLdsBM * p.ld_h * hsz < 0x7FFFFFFFu;
 }
 
-template <int FMT>
-static hipError_t launch_lds_fmt(const GemmParams& p, int stage, hipStream_t s) {
+template <int FMT, bool EPI>
+static hipError_t launch_lds_fe(const GemmParams& p, int stage, hipStream_t s) {
   if (stage == 1) {
     const dim3 grid((unsigned)(p.max_blocks * (p.I / 128)));
-    return launch_gemm_kernel(gemm_lds_stage1_kernel<FMT>, grid, dim3(kLdsThreads), s, p);
+    return launch_gemm_kernel(gemm_lds_stage1_kernel<FMT, EPI>, grid, dim3(kLdsThreads), s, p);
   }
   // persistent: one workgroup per CU (an XCD has 32), no more than the
   // largest queue has items
@@ -617,8 +626,13 @@ static hipError_t launch_lds_fmt(const GemmParams& p, int stage, hipStream_t s) 
   const int groups = ((n64 + kNumXcd - 1) / kNumXcd + 3) / 4;
   long long per_xcd = (long long)p.max_blocks * groups;
   if (per_xcd > 32) per_xcd = 32;
-  return launch_gemm_kernel(gemm_lds_accum_kernel<FMT>, dim3((unsigned)(kNumXcd * per_xcd)), dim3(kLdsThreads), s,
-                            p);
+  return launch_gemm_kernel(gemm_lds_accum_kernel<FMT, EPI>, dim3((unsigned)(kNumXcd * per_xcd)), dim3(kLdsThreads),
+                            s, p);
+}
+
+template <int FMT>
+static hipError_t launch_lds_fmt(const GemmParams& p, int stage, hipStream_t s) {
+  return epi_general(p, stage) ? launch_lds_fe<FMT, true>(p, stage, s) : launch_lds_fe<FMT, false>(p, stage, s);
 }
 
 hipError_t launch_gemm_lds(const GemmParams& p, int stage, int fmt, hipStream_t s) {

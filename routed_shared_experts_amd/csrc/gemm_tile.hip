@@ -2,7 +2,8 @@
 //
 // Stage 1 computes a = x_gathered . W13[e]^T, applies the per-token and
 // per-expert scales to the fp32 accumulator (MX-32 block scales inside the
-// block-scaled MFMA), then h = SiLU(a_gate) * a_up, rounded or quantised to
+// block-scaled MFMA), adds the expert's bias, then h = act(a_gate) * a_up
+// (SiLU or GELU), rounded or quantised to
 // the stage-2 input format (AITER PR 6106, "Technical Details"; vLLM PR 65207,
 // "Purpose", commit 2 for the two-stage structure).  Stage 2 computes
 // o = h . W2[e]^T with the same scale rules and hands the weighted pair rows to
@@ -118,7 +119,7 @@ __device__ __forceinline__ int lds_chunk_off(int r, int c) {
 // wave_ok = false take part in the staging and barriers but store nothing.
 // Starts by filling the row tables (the caller synchronises before reusing
 // the shared memory).
-template <int FMT, int STAGE, int NB>
+template <int FMT, int STAGE, int NB, bool EPI>
 __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB>& sm, int b, const ExpertView& ev,
                                            int c0, bool wave_ok, int cslot, bool group_count) {
   constexpr int esz = FmtInfo<FMT>::esz;
@@ -408,12 +409,15 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
       const size_t slot = (size_t)b * BM + r;
       const float sc = sm.rs[r] * ev.wscale;
       uint16_t* dst = reinterpret_cast<uint16_t*>(p.h) + slot * p.ld_h + c0 + 4 * (lane / 32);
+      const int cb = c0 + 4 * (lane / 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t bits[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          bits[v] = f32_to_bf16(silu_mul(acc32[0][nn][4 * j + v] * sc, acc32[1][nn][4 * j + v] * sc));
+          bits[v] = f32_to_bf16(epi_act<EPI>(acc32[0][nn][4 * j + v] * sc + epi_bias<EPI>(ev.bg, cb + 8 * j + v, ev.width),
+                                        acc32[1][nn][4 * j + v] * sc + epi_bias<EPI>(ev.bu, cb + 8 * j + v, ev.width),
+                                        p.act));
         *reinterpret_cast<uint2*>(dst + 8 * j) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
       }
     }
@@ -428,7 +432,11 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) hv[m][v] = silu_mul(acc[m][nb][v] * sc, acc[m + 2][nb][v] * sc);
+        for (int v = 0; v < 4; ++v) {
+          const int col = c0 + 4 * g + 16 * m + v;
+          hv[m][v] = epi_act<EPI>(acc[m][nb][v] * sc + epi_bias<EPI>(ev.bg, col, ev.width),
+                             acc[m + 2][nb][v] * sc + epi_bias<EPI>(ev.bu, col, ev.width), p.act);
+        }
       if constexpr (fmt_mx(FMT)) {
         // the wave's 32 columns are one MX-32 block of the token's h row
         float amax = 0.f;
@@ -487,14 +495,19 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
         if (tok < 0) continue;
         const float sc = sm.rs[r] * ev.wscale;
         const float gm = p.gamma ? p.gamma[tok] : 1.0f;
-        float* dst = p.acc + (size_t)tok * p.H + c0 + 4 * (lane / 32);
+        const int cb = c0 + 4 * (lane / 32);
+        float* dst = p.acc + (size_t)tok * p.H + cb;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
+            const int col = cb + 32 * mm + 8 * j;
             *reinterpret_cast<float4*>(dst + 32 * mm + 8 * j) =
-                make_float4(gm * (acc32[mm][nn][4 * j] * sc), gm * (acc32[mm][nn][4 * j + 1] * sc),
-                            gm * (acc32[mm][nn][4 * j + 2] * sc), gm * (acc32[mm][nn][4 * j + 3] * sc));
+                make_float4(gm * (acc32[mm][nn][4 * j] * sc + epi_bias<EPI>(ev.b2, col)),
+                            gm * (acc32[mm][nn][4 * j + 1] * sc + epi_bias<EPI>(ev.b2, col + 1)),
+                            gm * (acc32[mm][nn][4 * j + 2] * sc + epi_bias<EPI>(ev.b2, col + 2)),
+                            gm * (acc32[mm][nn][4 * j + 3] * sc + epi_bias<EPI>(ev.b2, col + 3)));
+          }
       }
       return;
     }
@@ -507,10 +520,14 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
         const float sc = sm.rs[r] * ev.wscale;
         const float gm = p.gamma ? p.gamma[tok] : 1.0f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          *reinterpret_cast<float4*>(p.acc + (size_t)tok * p.H + c0 + mb * 16 + 4 * g) =
-              make_float4(gm * (acc[mb][nb][0] * sc), gm * (acc[mb][nb][1] * sc), gm * (acc[mb][nb][2] * sc),
-                          gm * (acc[mb][nb][3] * sc));
+        for (int mb = 0; mb < 4; ++mb) {
+          const int col = c0 + mb * 16 + 4 * g;
+          *reinterpret_cast<float4*>(p.acc + (size_t)tok * p.H + col) =
+              make_float4(gm * (acc[mb][nb][0] * sc + epi_bias<EPI>(ev.b2, col)),
+                          gm * (acc[mb][nb][1] * sc + epi_bias<EPI>(ev.b2, col + 1)),
+                          gm * (acc[mb][nb][2] * sc + epi_bias<EPI>(ev.b2, col + 2)),
+                          gm * (acc[mb][nb][3] * sc + epi_bias<EPI>(ev.b2, col + 3)));
+        }
       }
       return;
     }
@@ -551,7 +568,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            acc32[mm][nn][v] = wgt * (acc32[mm][nn][v] * sc);
+            acc32[mm][nn][v] = wgt * (acc32[mm][nn][v] * sc + epi_bias<EPI>(ev.b2, c0 + 32 * mm + 8 * (v / 4) + 4 * h + v % 4));
             amax = tile_amax(amax, acc32[mm][nn][v]);
           }
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
@@ -580,7 +597,7 @@ __device__ __forceinline__ void tile_block(const GemmParams& p, TileSmem<16 * NB
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            acc[mb][nb][v] = wgt * (acc[mb][nb][v] * sc);
+            acc[mb][nb][v] = wgt * (acc[mb][nb][v] * sc + epi_bias<EPI>(ev.b2, c0 + 16 * mb + 4 * g + v));
             amax = tile_amax(amax, acc[mb][nb][v]);
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
@@ -722,7 +739,7 @@ constexpr int tile_waves_per_eu() {
 
 // Stage 1 (and the dense STORE stage 2): one workgroup per (block, column
 // tile) of 128 h columns / 256 output columns.
-template <int FMT, int STAGE, int NB>
+template <int FMT, int STAGE, int NB, bool EPI>
 __global__ __launch_bounds__(kTileThreads)
 __attribute__((amdgpu_waves_per_eu(tile_waves_per_eu<FMT, STAGE, NB>(), tile_waves_per_eu<FMT, STAGE, NB>())))
 void gemm_tile_kernel(GemmParams p) {
@@ -748,7 +765,7 @@ void gemm_tile_kernel(GemmParams p) {
   int c0 = n0 + wv * ((STAGE == 1) ? 32 : 64);
   const bool wave_ok = (STAGE == 1) ? (c0 < ev.width) : true;
   if (!wave_ok) c0 = 0;  // rows past a narrow chunk: read block 0, store nothing
-  tile_block<FMT, STAGE, NB>(p, sm, b, ev, c0, wave_ok, 0, false);
+  tile_block<FMT, STAGE, NB, EPI>(p, sm, b, ev, c0, wave_ok, 0, false);
 }
 
 // Stage 2 ACCUMULATE: persistent workgroups draining the per-XCD queues.
@@ -758,7 +775,7 @@ void gemm_tile_kernel(GemmParams p) {
 // once for the group on the counter (token, x) (x * groups + j < H/64 for
 // every non-empty group), among the T * (H/64) counter words.  Queue state
 // (next item, owner) follows the counters and is zero on entry.
-template <int FMT, int NB>
+template <int FMT, int NB, bool EPI>
 __global__ __launch_bounds__(kTileThreads)
 __attribute__((amdgpu_waves_per_eu(tile_waves_per_eu<FMT, 2, NB>(), tile_waves_per_eu<FMT, 2, NB>())))
 void gemm_tile_accum_kernel(GemmParams p) {
@@ -800,7 +817,7 @@ void gemm_tile_accum_kernel(GemmParams p) {
       const int t = q + kNumXcd * (4 * j + wv);
       const bool wave_ok = t < n64;
       const ExpertView ev = resolve_expert<FMT, 2>(p, e);
-      tile_block<FMT, 2, NB>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok, q * groups_q + j, group_count);
+      tile_block<FMT, 2, NB, EPI>(p, sm, b, ev, wave_ok ? 64 * t : 0, wave_ok, q * groups_q + j, group_count);
       __syncthreads();  // the next item rewrites the row tables
     }
   }
@@ -825,8 +842,8 @@ bool tile_kernel_fits(const GemmParams& p, int stage, int fmt) {
   return (size_t)p.max_blocks * p.block_m * p.ld_h * hsz < 0x7FFFFFFFu;
 }
 
-template <int FMT, int STAGE, int NB>
-static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
+template <int FMT, int STAGE, int NB, bool EPI>
+static hipError_t launch_tile_nbe(const GemmParams& p, hipStream_t s) {
   if (STAGE == 2 && p.mode != 0) {
     // persistent: as many workgroups per CU of each XCD as the register
     // allocation allows (an XCD has 32 CUs), no more than the largest queue
@@ -835,13 +852,18 @@ static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
     const int groups = ((n64 + kNumXcd - 1) / kNumXcd + 3) / 4;
     long long per_xcd = (long long)p.max_blocks * groups;
     if (per_xcd > 32 * tile_waves_per_eu<FMT, 2, NB>()) per_xcd = 32 * tile_waves_per_eu<FMT, 2, NB>();
-    return launch_gemm_kernel(gemm_tile_accum_kernel<FMT, NB>, dim3((unsigned)(kNumXcd * per_xcd)),
+    return launch_gemm_kernel(gemm_tile_accum_kernel<FMT, NB, EPI>, dim3((unsigned)(kNumXcd * per_xcd)),
                               dim3(kTileThreads), s, p);
   }
   constexpr int WCOLS = (STAGE == 1) ? 128 : 256;
   const int width_max = (STAGE == 1) ? (p.dense ? p.I_s : p.I) : p.H;
   const dim3 grid((unsigned)(p.max_blocks * (width_max / WCOLS)));
-  return launch_gemm_kernel(gemm_tile_kernel<FMT, STAGE, NB>, grid, dim3(kTileThreads), s, p);
+  return launch_gemm_kernel(gemm_tile_kernel<FMT, STAGE, NB, EPI>, grid, dim3(kTileThreads), s, p);
+}
+
+template <int FMT, int STAGE, int NB>
+static hipError_t launch_tile_nb(const GemmParams& p, hipStream_t s) {
+  return epi_general(p, STAGE) ? launch_tile_nbe<FMT, STAGE, NB, true>(p, s) : launch_tile_nbe<FMT, STAGE, NB, false>(p, s);
 }
 
 template <int FMT, int STAGE>

@@ -4,7 +4,7 @@
 // expert weights once and do almost no arithmetic per byte (vLLM PR 65207's
 // decode profile is this regime).  A workgroup here is a single wave that owns
 // NCG consecutive 16-column groups of one block: stage 1 owns 2 groups = 32 h
-// columns (one MX-32 block) and streams their gate and up rows, with SiLU-mul
+// columns (one MX-32 block) and streams their gate and up rows, with bias and act-mul
 // in registers; stage 2 owns 4 groups = one 64-column output tile and streams
 // those 64 rows of W2.  The weight rows are the MFMA M dimension and the
 // block's (at most 16) tokens the N dimension.  The K tile is the outer loop:
@@ -277,8 +277,12 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmParams p) {
 #pragma unroll
   for (int cgi = 0; cgi < NCG; ++cgi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      res[cgi][j] = (STAGE == 1) ? silu_mul(acc[cgi][0][j] * sc, acc[cgi][NW - 1][j] * sc) : acc[cgi][0][j] * sc;
+    for (int j = 0; j < 4; ++j) {
+      const int col = c0 + 16 * cgi + 4 * g + j;
+      res[cgi][j] = (STAGE == 1) ? act_mul(acc[cgi][0][j] * sc + bias_at(ev.bg, col, ev.width),
+                                           acc[cgi][NW - 1][j] * sc + bias_at(ev.bu, col, ev.width), p.act)
+                                 : acc[cgi][0][j] * sc + bias_at(ev.b2, col);
+    }
 
   if constexpr (STAGE == 1) {
     const size_t slot = (size_t)slot_l;

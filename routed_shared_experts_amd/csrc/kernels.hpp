@@ -61,6 +61,13 @@ struct GemmParams {
   const uint8_t* ws2;
   const void* ws13_s;
   const void* ws2_s;
+  // per-expert fp32 biases (or NULL): b13 [E][2I], b2 [E][H]; shared bs13
+  // [2 I_s], bs2 [H]
+  const float* b13;
+  const float* b2;
+  const float* bs13;
+  const float* bs2;
+  int act;  // stage-1 activation: 0 SiLU, 1 GELU (tanh form)
   const uint8_t* x;
   const void* x_s;
   int dense, block_m, max_blocks;
@@ -101,6 +108,12 @@ struct GemmParams {
   // (instrumentation; both NULL for an ordinary launch)
   hipEvent_t ev_start, ev_stop;
 };
+
+// Whether a stage needs the general epilogue (a bias, or an activation other
+// than SiLU).
+inline bool epi_general(const GemmParams& p, int stage) {
+  return stage == 1 ? (p.b13 || p.bs13 || p.act != 0) : (p.b2 || p.bs2);
+}
 
 // Launch of a GEMM kernel taking GemmParams; with instrumentation events the
 // dispatch itself records the kernel's start and end times on them.

@@ -7,7 +7,7 @@ aux-stream mode needs, and calls the library.
 
 import torch
 
-from . import (MoeForwardArgs, MoeWeights, MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1, MOE_SCALE_NONE,
+from . import (MoeForwardArgs, MoeWeights, ACTIVATIONS, MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1, MOE_SCALE_NONE,
                MOE_SCALE_PER_EXPERT, MOE_SCALE_MX32, MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID,
                MOE_LAYOUT_TILED, SHARED_MODES, MOE_OK, MoeError, moe_validate, moe_workspace_bytes,
                moe_forward, moe_pack_weights, moe_pack_mx_scales, moe_status_str, _ptr)
@@ -22,10 +22,11 @@ FORMATS = {
 }
 
 
-def weights_struct(w13, w2, s13, s2, fmt):
-    """Weight family struct; the tensors must already be in the tiled layout."""
+def weights_struct(w13, w2, s13, s2, fmt, b13=None, b2=None):
+    """Weight family struct; the tensors must already be in the tiled layout
+    (b13, b2: optional fp32 biases)."""
     _, wdt, wsc, _ = FORMATS[fmt]
-    return MoeWeights(_ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2), wdt, wsc, MOE_LAYOUT_TILED)
+    return MoeWeights(_ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2), wdt, wsc, MOE_LAYOUT_TILED, _ptr(b13), _ptr(b2))
 
 
 def pack_weights(cfg, inp, stream=None):
@@ -57,9 +58,12 @@ def forward_args(cfg, inp, out, shared_mode="auto", block_m=0, out_dtype=None):
     a.x = _ptr(inp["x"])
     a.x_dtype = xdt
     a.x_row_scale = _ptr(inp.get("x_scale"))
-    a.routed = weights_struct(inp["w13"], inp["w2"], inp.get("w13_scale"), inp.get("w2_scale"), cfg.fmt)
+    a.routed = weights_struct(inp["w13"], inp["w2"], inp.get("w13_scale"), inp.get("w2_scale"), cfg.fmt,
+                              inp.get("b13"), inp.get("b2"))
     if cfg.I_s > 0:
-        a.shared = weights_struct(inp["ws13"], inp["ws2"], inp.get("ws13_scale"), inp.get("ws2_scale"), cfg.fmt)
+        a.shared = weights_struct(inp["ws13"], inp["ws2"], inp.get("ws13_scale"), inp.get("ws2_scale"), cfg.fmt,
+                                  inp.get("bs13"), inp.get("bs2"))
+    a.activation = ACTIVATIONS[getattr(cfg, "activation", "silu")]
     a.gate_w = _ptr(inp.get("gate_w")) if cfg.gated else None
     a.shared_mode = SHARED_MODES[shared_mode] if cfg.I_s > 0 else SHARED_MODES["none"]
     a.block_m = block_m

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from gpu_util import TOL, inputs, run_forward, assert_close, compare
 
@@ -24,6 +25,22 @@ SMALL = {
                       topk_group=2, routed_scaling_factor=2.5, fmt="mxfp8", gated=False, bias_std=0.1),
     "small_a8w8": LC("small_a8w8", T=90, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                      topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    # per-expert biases on both stages, GELU or SiLU (general epilogue of every kernel family)
+    "small_bias_gelu_bf16": LC("small_bias_gelu_bf16", T=90, H=256, E=16, I=128, I_s=256, topk=4, fmt="bf16",
+                               bias13_std=0.2, bias2_std=0.01, activation="gelu_tanh"),
+    "small_bias_mxfp8": LC("small_bias_mxfp8", T=70, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid",
+                           n_group=4, topk_group=2, fmt="mxfp8", gated=False, bias_std=0.1, bias13_std=0.3,
+                           bias2_std=0.03),
+    "small_bias_gelu_a8w8": LC("small_bias_gelu_a8w8", T=90, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid",
+                               n_group=4, topk_group=2, fmt="a8w8", gated=False, bias13_std=0.3, bias2_std=0.04,
+                               activation="gelu_tanh"),
+    "small_bias_gelu_mxfp4": LC("small_bias_gelu_mxfp4", T=70, H=512, E=16, I=256, I_s=512, topk=4,
+                                score="sigmoid", n_group=4, topk_group=2, fmt="mxfp4", gated=False, bias_std=0.1,
+                                bias13_std=0.3, bias2_std=0.03, activation="gelu_tanh"),
+    "tiny_bias_gelu_f32": LC("tiny_bias_gelu_f32", T=8, H=64, E=4, I=32, I_s=64, topk=2, fmt="f32",
+                             logits="linear", bias13_std=0.1, bias2_std=0.001, activation="gelu_tanh"),
+    "decode_bias_gelu_bf16": LC("decode_bias_gelu_bf16", T=24, H=512, E=16, I=256, I_s=256, topk=4, fmt="bf16",
+                                bias13_std=0.2, bias2_std=0.01, activation="gelu_tanh"),
     # softmax scores with grouped top-k (routing in its own launch)
     "small_softmax_groups": LC("small_softmax_groups", T=80, H=256, E=32, I=128, I_s=128, topk=6,
                                score="softmax", n_group=8, topk_group=3, fmt="bf16"),
@@ -52,8 +69,16 @@ def test_small_layers_all_outputs(gpu, name, mode, block_m):
         pytest.skip("per-row fp8 intermediate needs a single pseudo chunk")
     inp = inputs(cfg, gpu)
     out, _ = run_forward(cfg, inp, mode, block_m=block_m)
-    rel, floor, _ = assert_close(cfg, out, inp)
+    rel, floor, r = assert_close(cfg, out, inp)
     print(f"{name}/{mode}/bm{block_m}: max|err|/rms={rel:.3e} floor={floor:.3e}")
+    if (cfg.bias13_std or cfg.bias2_std) and mode == "pseudo" and block_m == 0:
+        # the check has teeth: dropping either bias moves the output by much
+        # more than the tolerance
+        host = workloads.to_host(inp)
+        rms = np.sqrt((r["y"] ** 2).mean())
+        for drop in (("b13", "bs13"), ("b2", "bs2")):
+            y0 = oracle.moe_layer(dict(host, **{k: None for k in drop}), cfg)["y"]
+            assert np.abs(y0 - r["y"]).max() / rms > 5 * TOL[cfg.fmt], drop
 
 
 @pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])

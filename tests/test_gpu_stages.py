@@ -31,6 +31,8 @@ CASES = {
                topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
     "mxfp4": LC("steps_mxfp4", T=70, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                 topk_group=2, fmt="mxfp4", gated=False, bias_std=0.1),
+    "bias_gelu_bf16": LC("steps_bias_gelu_bf16", T=100, H=256, E=8, I=128, I_s=256, topk=2, fmt="bf16",
+                         logits="iid", bias13_std=0.2, bias2_std=0.01, activation="gelu_tanh"),
 }
 
 DENSE_BM = 64
@@ -86,9 +88,12 @@ def run_steps(cfg, inp, mode, block_m, dev):
     def base_args():
         a = m.MoeStageArgs()
         a.T, a.H, a.E, a.I, a.I_s = T, H, E, I, Is
-        a.routed = weights_struct(W["w13"], W["w2"], W.get("w13_scale"), W.get("w2_scale"), cfg.fmt)
-        a.shared = weights_struct(W["ws13"], W["ws2"], W.get("ws13_scale"), W.get("ws2_scale"), cfg.fmt)
+        a.routed = weights_struct(W["w13"], W["w2"], W.get("w13_scale"), W.get("w2_scale"), cfg.fmt,
+                                  W.get("b13"), W.get("b2"))
+        a.shared = weights_struct(W["ws13"], W["ws2"], W.get("ws13_scale"), W.get("ws2_scale"), cfg.fmt,
+                                  W.get("bs13"), W.get("bs2"))
         a.x, a.x_scale = _ptr(x), _ptr(x_scale)
+        a.activation = m.ACTIVATIONS[cfg.activation]
         return a
 
     out = torch.empty((T, H), dtype=torch.float32 if odt == m.MOE_F32 else torch.bfloat16, device=dev)

@@ -56,6 +56,9 @@ class LayerConfig:
     bias_std: float = 0.0
     logits: str = "iid"          # 'linear' | 'iid' | 'zipf'
     zipf_s: float = 0.0
+    bias13_std: float = 0.0      # std of the per-expert fp32 stage-1 biases b13, bs13 (0: none)
+    bias2_std: float = 0.0       # std of the per-expert fp32 stage-2 biases b2, bs2 (0: none)
+    activation: str = "silu"     # 'silu' | 'gelu_tanh'
 
     def replace(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -216,6 +219,17 @@ def generate(cfg, device="cpu"):
         inp["ws2_scale"] = None if s2 is None else (s2[0] if mx else s2)
     else:
         inp["ws13"] = inp["ws2"] = inp["ws13_scale"] = inp["ws2_scale"] = None
+    # per-expert biases (fp32): b13 [E, 2I], b2 [E, H]; shared bs13 [2 I_s], bs2 [H]
+    for k in ("b13", "b2", "bs13", "bs2"):
+        inp[k] = None
+    if cfg.bias13_std > 0:
+        inp["b13"] = _randn((E, 2 * I), device, cfg.name, "b13") * cfg.bias13_std
+        if I_s > 0:
+            inp["bs13"] = _randn((2 * I_s,), device, cfg.name, "bs13") * cfg.bias13_std
+    if cfg.bias2_std > 0:
+        inp["b2"] = _randn((E, H), device, cfg.name, "b2") * cfg.bias2_std
+        if I_s > 0:
+            inp["bs2"] = _randn((H,), device, cfg.name, "bs2") * cfg.bias2_std
     return inp
 
 
