@@ -117,7 +117,8 @@ typedef enum {
   MOE_FEATURE_BF16 = 7,
   MOE_FEATURE_MXFP4 = 8,
   MOE_FEATURE_EXPERT_BIAS = 9, /* per-expert bias on the stage-1 and stage-2 accumulators */
-  MOE_FEATURE_GELU_TANH = 10   /* MOE_ACT_GELU_TANH */
+  MOE_FEATURE_GELU_TANH = 10,  /* MOE_ACT_GELU_TANH */
+  MOE_FEATURE_ROUTER_GEMM = 11 /* moe_forward_args.router_w: logits computed in the prologue */
 } moe_feature;
 
 /* Weight layout.  Logically every weight matrix is row-major: rows = output
@@ -190,6 +191,12 @@ typedef struct {
    * the kernels' own dispatch) */
   hipEvent_t* timing_events;
   int32_t activation; /* moe_activation of routed and shared experts (0 = SILU) */
+  /* optional router projection [E][H], row-major (F32 when x is F32, else
+   * BF16; F32 accumulation): when not NULL the layer computes the router
+   * logits x . router_w^T itself, in the routing launch (A8W8: from the
+   * dequantised codes, code * x_row_scale), and logits is not read (may be
+   * NULL) */
+  const void* router_w;
 } moe_forward_args;
 
 /* Pure host check of a forward request; makes no HIP call.  Returns MOE_OK,
@@ -285,6 +292,18 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
 moe_status shared_gate_dot(const void* x, int32_t x_dtype, const void* g, int32_t T,
                            int32_t H, int32_t apply_sigmoid, float* gate_out,
                            hipStream_t stream);
+
+/* Router logits l = x . router_w^T (the projection in front of the routing
+ * of vLLM PR 65207, "Purpose", commit 1; the same matrix-core kernel the
+ * fused prologue of moe_forward runs, without the routing).
+ * x [T][H] in x_dtype: F32 (router_w F32), BF16 (router_w BF16) or FP8_E4M3
+ * codes with x_row_scale [T] fp32 (router_w BF16; l = scale_t * codes . w);
+ * router_w [E][H] row-major; logits [T][E] fp32 out.  H % 64 == 0 (% 32 for
+ * F32), E <= 512, pointers 16-byte aligned (x_row_scale 4).  Errors:
+ * MOE_ERR_INVALID_ARG for bad shapes or pointers, MOE_ERR_UNSUPPORTED for
+ * another x_dtype, MOE_ERR_HIP for a failed launch. */
+moe_status moe_router_logits(const void* x, int32_t x_dtype, const float* x_row_scale, const void* router_w,
+                             int32_t T, int32_t H, int32_t E, float* logits, hipStream_t stream);
 
 /* In-layer MX-32 quantisation of bf16 activations (OCP MX v1.0; AITER PR
  * 6106, "Technical Details": 32-element K blocks, K % 32 == 0): per block of

@@ -64,6 +64,7 @@ from .routing import route
 from .sorting import sort_tokens
 from .layer import (
     gate,
+    router_logits,
     decode_activations,
     expert_weights,
     shared_weights,
@@ -77,7 +78,7 @@ __all__ = [
     "bf16_bits_to_f64", "round_to_bf16_bits", "e4m3_decode", "e4m3_encode_rne_sat",
     "e8m0_decode", "mx_quantize", "mx_dequantize", "row_quantize_e4m3", "e2m1_decode", "e2m1_unpack",
     "mx4_dequantize",
-    "spec_exp", "spec_sigmoid", "route", "sort_tokens", "gate",
+    "spec_exp", "spec_sigmoid", "route", "sort_tokens", "gate", "router_logits",
     "decode_activations", "expert_weights", "shared_weights", "expert_mlp", "activation",
     "moe_layer", "stage1_reference",
 ]

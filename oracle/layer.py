@@ -86,6 +86,17 @@ def gate_input(inp, fmt):
     return _decode_plain(inp["x"], fmt)
 
 
+def router_logits(inp, fmt):
+    """Router logits l = x . Wr^T in float64 from the layer input as real
+    numbers (a8w8: codes times the token's scale; MX formats: the bf16 input
+    before its in-layer quantisation) and the router projection Wr [E, H]
+    (fp32 for the f32 format, else bf16) -- the projection in front of the
+    routing (vLLM PR 65207, Purpose, commit 1)."""
+    wr = inp["router_w"]
+    W = np.asarray(wr, np.float32).astype(np.float64) if fmt == "f32" else bf16_bits_to_f64(wr)
+    return gate_input(inp, fmt) @ W.T
+
+
 def gate(x, g):
     """gamma_t = sigmoid(sum_h x_th g_h), the dot product in float64."""
     z = np.asarray(x, np.float64) @ np.asarray(g, np.float64)
@@ -180,8 +191,13 @@ def _expert_bias(inp, e):
 
 
 def route_layer(inp, prm, gamma=None, n_pseudo=0):
-    """Routing of the layer (ids, weights) with the layer's parameters."""
-    return route(inp["logits"], topk=prm.topk, score=prm.score, bias=inp.get("bias"),
+    """Routing of the layer (ids, weights) with the layer's parameters; the
+    logits are the input's, or, when the layer is given its router projection
+    instead, router_logits rounded to fp32 (the logits' type in the layer)."""
+    logits = inp.get("logits")
+    if logits is None:
+        logits = router_logits(inp, prm.fmt).astype(np.float32)
+    return route(logits, topk=prm.topk, score=prm.score, bias=inp.get("bias"),
                  n_group=prm.n_group, topk_group=prm.topk_group,
                  group_score_topk=prm.group_score_topk, renormalize=prm.renormalize,
                  routed_scaling_factor=prm.routed_scaling_factor,

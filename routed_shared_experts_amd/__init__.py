@@ -31,14 +31,15 @@ MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_TILED = 0, 1
 MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 (MOE_FEATURE_ACCUMULATE_OUTPUT, MOE_FEATURE_PSEUDO_SHARED, MOE_FEATURE_AUX_STREAM,
  MOE_FEATURE_MXFP8, MOE_FEATURE_A8W8, MOE_FEATURE_F32, MOE_FEATURE_BF16, MOE_FEATURE_MXFP4,
- MOE_FEATURE_EXPERT_BIAS, MOE_FEATURE_GELU_TANH) = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+ MOE_FEATURE_EXPERT_BIAS, MOE_FEATURE_GELU_TANH, MOE_FEATURE_ROUTER_GEMM) = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11
 ACTIVATIONS = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 
 SHARED_MODES = {"none": MOE_SHARED_NONE, "pseudo": MOE_SHARED_PSEUDO, "aux": MOE_SHARED_AUX,
                 "auto": MOE_SHARED_AUTO}
 
 # Exported symbols, in the order of include/moe.h.
-EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_route", "shared_gate_dot",
+EXPORTS = ["moe_validate", "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_route", "moe_router_logits",
+           "shared_gate_dot",
            "moe_quant_mx", "moe_sort_capacity", "moe_sort_scratch_bytes", "moe_pack_weights", "moe_pack_mx_scales",
            "moe_sort_tokens", "moe_stage1", "moe_stage2_accum", "moe_query_feature", "moe_status_str",
            "moe_last_hip_error"]
@@ -60,7 +61,8 @@ class MoeForwardArgs(ctypes.Structure):
                 ("x", c_void_p), ("x_dtype", c_int32), ("x_row_scale", c_void_p),
                 ("routed", MoeWeights), ("shared", MoeWeights), ("gate_w", c_void_p),
                 ("shared_mode", c_int32), ("block_m", c_int32), ("out", c_void_p),
-                ("out_dtype", c_int32), ("timing_events", c_void_p), ("activation", c_int32)]
+                ("out_dtype", c_int32), ("timing_events", c_void_p), ("activation", c_int32),
+                ("router_w", c_void_p)]
 
 
 class MoeStageArgs(ctypes.Structure):
@@ -99,6 +101,8 @@ def _load():
         "moe_forward_noalloc": (c_int32, [P(MoeForwardArgs), c_void_p, c_void_p, c_void_p, c_void_p]),
         "moe_route": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                 c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "moe_router_logits": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                        c_void_p, c_void_p]),
         "shared_gate_dot": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                       c_void_p]),
         "moe_quant_mx": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
@@ -163,6 +167,18 @@ def moe_validate(args):
 
 def moe_workspace_bytes(args):
     return int(_lib.moe_workspace_bytes(ctypes.byref(args)))
+
+
+def moe_router_logits(x, router_w, logits, x_row_scale=None, stream=None):
+    """logits [T, E] fp32 = x . router_w^T (x fp32 / bf16 / float8_e4m3fn codes
+    with x_row_scale; router_w [E, H] fp32 for fp32 x, else bf16)."""
+    import torch
+    T, H = x.shape
+    E = router_w.shape[0]
+    xdt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}.get(x.dtype, MOE_FP8_E4M3)
+    st = _lib.moe_router_logits(_ptr(x), xdt, _ptr(x_row_scale), _ptr(router_w), T, H, E, _ptr(logits),
+                                _stream(stream))
+    _check(st, "moe_router_logits")
 
 
 def moe_route(logits, topk_ids, topk_w, *, topk, bias=None, n_group=1, topk_group=1, group_score_topk=2,

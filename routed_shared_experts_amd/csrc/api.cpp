@@ -85,6 +85,7 @@ struct Plan {
   // routing ids themselves (block b = sb * E_total + e), so no sort launch runs
   int self_sort, ss_blocks, h_rows;
   int dense_bm, dense_blocks;
+  size_t off_logits;  // router logits [T][E] fp32 when the layer computes them
   size_t off_ids, off_w, off_gamma, off_xq, off_xs, off_counts, off_offsets, off_nblk, off_sorted, off_sortws,
       off_bexp, off_h, off_hs, off_hsh, off_hshs, off_amax_sh, off_acc, off_pair, off_cnt, off_amax, off_end;
   size_t zero_begin, zero_end;  // region the sort launch clears
@@ -120,8 +121,9 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (a->group_score_topk != 1 && a->group_score_topk != 2) return MOE_ERR_INVALID_ARG;
   if (a->n_group > 1 && a->group_score_topk == 2 && a->E / a->n_group < 2) return MOE_ERR_INVALID_ARG;
   if ((long long)a->topk > (long long)a->topk_group * (a->E / a->n_group)) return MOE_ERR_INVALID_ARG;
-  if (a->T > 0 && (!a->logits || !a->x || !a->out)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(a->logits) || !aligned16(a->x) || !aligned16(a->out)) return MOE_ERR_INVALID_ARG;
+  if (a->T > 0 && ((!a->logits && !a->router_w) || !a->x || !a->out)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a->logits) || !aligned16(a->x) || !aligned16(a->out) || !aligned16(a->router_w))
+    return MOE_ERR_INVALID_ARG;
   if (a->bias && ((uintptr_t)a->bias & 3u)) return MOE_ERR_INVALID_ARG;
   if (a->bias && a->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (a->out_dtype != MOE_F32 && a->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -147,6 +149,7 @@ moe_status validate_impl(const moe_forward_args* a, int* fmt_out) {
   if (a->H % kt || a->I % kt || (a->I_s % kt)) return MOE_ERR_INVALID_ARG;
   if (a->H % 64) return MOE_ERR_INVALID_ARG;  // stage-2 column tile
   if (fmt == FMT_MX4 && !mx4_shapes_ok(a->H, a->I, a->I_s)) return MOE_ERR_INVALID_ARG;
+  if (a->router_w && a->H % (a->x_dtype == MOE_F32 ? 32 : 64)) return MOE_ERR_INVALID_ARG;
   if (a->gate_w) {
     if (!aligned16(a->gate_w)) return MOE_ERR_INVALID_ARG;
     if (fmt != FMT_F32 && fmt != FMT_BF16) return MOE_ERR_UNSUPPORTED;
@@ -211,6 +214,7 @@ Plan make_plan(const moe_forward_args* a, int fmt) {
   const int esz_h = h_elem_bytes(fmt);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
+  pl.off_logits = take(a->router_w ? (size_t)a->T * a->E * 4 : 0);
   pl.off_ids = take((size_t)P * 4);
   pl.off_w = take((size_t)P * 4);
   pl.off_gamma = take((size_t)a->T * 4);
@@ -356,7 +360,8 @@ int32_t moe_query_feature(int32_t feature) {
     case MOE_FEATURE_F32:
     case MOE_FEATURE_BF16:
     case MOE_FEATURE_EXPERT_BIAS:
-    case MOE_FEATURE_GELU_TANH: return 1;
+    case MOE_FEATURE_GELU_TANH:
+    case MOE_FEATURE_ROUTER_GEMM: return 1;
     default: return 0;
   }
 }
@@ -415,6 +420,30 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
   p.do_route = 1;
   clear_pending_error();
   HIP_TRY(launch_route(p, stream));
+  return MOE_OK;
+}
+
+moe_status moe_router_logits(const void* x, int32_t x_dtype, const float* x_row_scale, const void* router_w,
+                             int32_t T, int32_t H, int32_t E, float* logits, hipStream_t stream) {
+  if (T < 0 || H <= 0 || E <= 0 || E > 512) return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (H % (x_dtype == MOE_F32 ? 32 : 64)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !logits || !aligned16(x) || !aligned16(router_w) || !aligned16(logits))
+    return MOE_ERR_INVALID_ARG;
+  if (x_dtype == MOE_FP8_E4M3 && (!x_row_scale || ((uintptr_t)x_row_scale & 3u))) return MOE_ERR_INVALID_ARG;
+  RouterParams rg{};
+  rg.x = x;
+  rg.x_fmt = x_dtype == MOE_F32 ? 0 : (x_dtype == MOE_BF16 ? 1 : 2);
+  rg.x_scale = x_row_scale;
+  rg.w = router_w;
+  rg.T = T;
+  rg.H = H;
+  rg.E = E;
+  rg.logits = logits;
+  RouteParams rp{};  // do_route = 0: logits only
+  clear_pending_error();
+  HIP_TRY(launch_router(rg, rp, stream));
   return MOE_OK;
 }
 
@@ -680,10 +709,26 @@ moe_status moe_forward(const moe_forward_args* a, void* workspace, size_t worksp
   // groups) and nothing else in the prologue that stage 1 reads (no MX
   // quantisation of x, no a8w8 row maxima to clear) runs the routing inside
   // its own launch; the aux stream needs gamma before stage 1, so not with it.
-  const bool fuse_route = pl.self_sort && !aux && a->score == MOE_SCORE_SOFTMAX && a->n_group <= 1 &&
-                          (fmt == FMT_BF16 || fmt == FMT_F32) && a->E <= 64 && a->E % 4 == 0 &&
+  // With router weights the logits come from the router GEMM, which routes
+  // its tokens in the same launch.
+  const bool fuse_route = !a->router_w && pl.self_sort && !aux && a->score == MOE_SCORE_SOFTMAX &&
+                          a->n_group <= 1 && (fmt == FMT_BF16 || fmt == FMT_F32) && a->E <= 64 && a->E % 4 == 0 &&
                           aligned16(a->logits);
-  if (!fuse_route) HIP_TRY(launch_route(rp, main_s));
+  if (a->router_w) {
+    RouterParams rg{};
+    rg.x = a->x;
+    rg.x_fmt = a->x_dtype == MOE_F32 ? 0 : (a->x_dtype == MOE_BF16 ? 1 : 2);
+    rg.x_scale = a->x_row_scale;
+    rg.w = a->router_w;
+    rg.T = a->T;
+    rg.H = a->H;
+    rg.E = a->E;
+    rg.logits = reinterpret_cast<float*>(ws + pl.off_logits);
+    rp.logits = rg.logits;
+    HIP_TRY(launch_router(rg, rp, main_s));
+  } else if (!fuse_route) {
+    HIP_TRY(launch_route(rp, main_s));
+  }
   if (tev) HIP_TRY(hipEventRecord(tev[1], main_s));
 
   GemmParams g{};

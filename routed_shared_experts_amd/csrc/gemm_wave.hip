@@ -73,7 +73,7 @@ __device__ __forceinline__ void fused_route_wave(const GemmParams& p, int first,
     clear_region(p.route.zero_ptr, p.route.zero_vec, first + p.route.T);
     return;
   }
-  route_token<1>(p.route, w, lane, sel, val);
+  route_token<1>(p.route, w, lane, sel, val, p.route.logits + (size_t)w * p.route.E);
 }
 
 template <int FMT, int STAGE, int D>

@@ -38,6 +38,18 @@ struct RouteParams {
   long long zero_vec;
 };
 
+// Router-logit GEMM: logits [T][E] = x . w^T (fp32 accumulation); x_fmt 0:
+// fp32 x and w; 1: bf16 x and w; 2: e4m3 x with an fp32 scale per token,
+// bf16 w.  w is row-major [E][H].
+struct RouterParams {
+  const void* x;
+  int x_fmt;
+  const float* x_scale;
+  const void* w;
+  int T, H, E;
+  float* logits;
+};
+
 struct SortParams {
   const int32_t* ids;
   int P, n_experts, block_m, capacity;
@@ -127,6 +139,9 @@ inline hipError_t launch_gemm_kernel(K kernel, dim3 grid, dim3 block, hipStream_
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
+// the router GEMM, then (rp.do_route) the routing of RouteParams from the
+// computed logits in the same launch (rp.logits is not read)
+hipError_t launch_router(const RouterParams& g, const RouteParams& rp, hipStream_t s);
 hipError_t launch_gate_dot(const void* x, int x_f32, const void* g, int T, int H, int apply_sigmoid,
                            float* out, hipStream_t s);
 hipError_t launch_sort(const SortParams& p, hipStream_t s);

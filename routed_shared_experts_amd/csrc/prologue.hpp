@@ -109,12 +109,13 @@ __device__ __forceinline__ void mx_quant_row(const uint16_t* xr, int H, uint8_t*
 }
 
 // Token t by one wave.  sel / val: this wave's LDS scratch of at least E
-// floats.  NPL = experts per lane (E <= 64 * NPL).
+// floats; lrow: the token's E router logits (global memory or LDS).  NPL =
+// experts per lane (E <= 64 * NPL).
 template <int NPL>
-__device__ __forceinline__ void route_token(const RouteParams& p, int t, int lane, float* sel, float* val) {
+__device__ __forceinline__ void route_token(const RouteParams& p, int t, int lane, float* sel, float* val,
+                                            const float* lrow) {
   const int E = p.E;
   // the logits first: their loads overlap the gate dot
-  const float* lrow = p.logits + (size_t)t * E;
   float lg[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_kernel(RouteParams p
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * kRouteWaves + wv;
   if (t >= p.T) return;
-  route_token<NPL>(p, t, lane, s_sel[wv], s_val[wv]);
+  route_token<NPL>(p, t, lane, s_sel[wv], s_val[wv], p.logits + (size_t)t * p.E);
 }
 
 // Standalone gate dot: one workgroup of 256 threads per token, any H.

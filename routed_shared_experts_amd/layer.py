@@ -53,7 +53,8 @@ def forward_args(cfg, inp, out, shared_mode="auto", block_m=0, out_dtype=None):
     a.n_group, a.topk_group, a.group_score_topk = cfg.n_group, cfg.topk_group, cfg.group_score_topk
     a.renormalize = int(bool(cfg.renormalize))
     a.routed_scaling_factor = float(cfg.routed_scaling_factor)
-    a.logits = _ptr(inp["logits"])
+    a.logits = _ptr(inp.get("logits"))
+    a.router_w = _ptr(inp.get("router_w"))
     a.bias = _ptr(inp.get("bias"))
     a.x = _ptr(inp["x"])
     a.x_dtype = xdt

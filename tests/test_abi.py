@@ -210,3 +210,24 @@ def test_step_entry_points_reject_bad_arguments():
     sa = m.MoeStageArgs()
     assert L.moe_stage1(ctypes.byref(sa), None) == m.MOE_ERR_INVALID_ARG
     assert L.moe_stage2_accum(None, None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_router_weights_replace_the_logits_input():
+    """With router weights the logits input may be NULL; the router GEMM's
+    shape and pointer rules are checked before any launch."""
+    c = workloads.CONFIGS["decode_bf16"]
+    rw = ctypes.c_void_p(0x7000000)
+    a = _args(c, logits=None, router_w=rw)
+    assert m.moe_validate(a) == m.MOE_OK
+    assert m.moe_workspace_bytes(a) >= m.moe_workspace_bytes(_args(c)) + c.T * c.E * 4
+    assert m.moe_validate(_args(c, logits=None)) == m.MOE_ERR_INVALID_ARG          # neither
+    assert m.moe_validate(_args(c, logits=None, router_w=ctypes.c_void_p(0x7000008))) == m.MOE_ERR_INVALID_ARG
+    L = m.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.moe_router_logits(p, m.MOE_BF16, None, p, 4, 96, 8, p, None) == m.MOE_ERR_INVALID_ARG   # H % 64
+    assert L.moe_router_logits(p, m.MOE_F32, None, p, 4, 80, 8, p, None) == m.MOE_ERR_INVALID_ARG    # H % 32
+    assert L.moe_router_logits(p, m.MOE_BF16, None, p, 4, 128, 513, p, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_router_logits(p, m.MOE_FP8_E4M3, None, p, 4, 128, 8, p, None) == m.MOE_ERR_INVALID_ARG  # scale
+    assert L.moe_router_logits(p, m.MOE_FP4_E2M1, None, p, 4, 128, 8, p, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_router_logits(None, m.MOE_BF16, None, None, 0, 128, 8, None, None) == m.MOE_OK      # empty
+    assert m.moe_query_feature(m.MOE_FEATURE_ROUTER_GEMM) == 1

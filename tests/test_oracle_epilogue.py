@@ -102,3 +102,34 @@ def test_stage1_bias_is_an_extra_input_column(fmt, act):
     # the comparison has teeth: the layer without the stage-1 bias is far off
     wrong = oracle.moe_layer(dict(host, b13=None, bs13=None), cfg)["y"]
     assert np.abs(wrong - y).max() > 10 * tol
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "mxfp8", "a8w8"])
+def test_router_logits_brute_force(fmt):
+    """oracle.router_logits against an explicit sum over k of x_tk w_ek from
+    the decoded inputs, on a tiny case (a8w8: the token's scale times the
+    codes; MX formats: the bf16 input before its quantisation)."""
+    cfg = workloads.LayerConfig(name=f"rl_{fmt}", T=3, H=64 if fmt != "a8w8" else 64, E=5, I=32, I_s=0, topk=2,
+                                fmt=fmt, gated=False, router_std=0.1)
+    host = workloads.to_host(workloads.generate(cfg))
+    got = oracle.router_logits(host, fmt)
+    if fmt == "f32":
+        x = host["x"].astype(np.float64)
+        w = host["router_w"].astype(np.float64)
+    else:
+        w = oracle.bf16_bits_to_f64(host["router_w"])
+        if fmt == "a8w8":
+            x = oracle.e4m3_decode(host["x"]) * host["x_scale"].astype(np.float64)[:, None]
+        else:
+            x = oracle.bf16_bits_to_f64(host["x"])
+    for t in range(cfg.T):
+        for e in range(cfg.E):
+            s = 0.0
+            for k in range(cfg.H):
+                s += x[t, k] * w[e, k]
+            assert abs(got[t, e] - s) <= 1e-12 * (np.abs(x[t]) @ np.abs(w[e]))
+    # the layer routes on these logits rounded to fp32 when it has no logits input
+    assert host["logits"] is None
+    ids, _ = oracle.route(got.astype(np.float32), topk=cfg.topk)
+    r = oracle.moe_layer(host, cfg)
+    assert np.array_equal(r["ids"], ids)

@@ -59,6 +59,8 @@ class LayerConfig:
     bias13_std: float = 0.0      # std of the per-expert fp32 stage-1 biases b13, bs13 (0: none)
     bias2_std: float = 0.0       # std of the per-expert fp32 stage-2 biases b2, bs2 (0: none)
     activation: str = "silu"     # 'silu' | 'gelu_tanh'
+    router_std: float = 0.0      # > 0: router projection [E, H] ~ N(0, std^2) in x's precision, and the
+                                 # layer computes its own logits (the logits input is then None)
 
     def replace(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -200,6 +202,11 @@ def generate(cfg, device="cpu"):
         inp["logits"] = _randn((T, E), device, cfg.name, "logits")
     else:
         inp["logits"] = _zipf_logits(cfg, device)
+    inp["router_w"] = None
+    if cfg.router_std > 0:
+        wr = _randn((E, H), device, cfg.name, "router_w") * cfg.router_std
+        inp["router_w"] = wr if cfg.fmt == "f32" else wr.to(torch.bfloat16)
+        inp["logits"] = None
     inp["bias"] = (_randn((E,), device, cfg.name, "bias") * cfg.bias_std) if cfg.bias_std > 0 else None
     if cfg.gated:
         gw = _randn((H,), device, cfg.name, "gate") * 0.02
