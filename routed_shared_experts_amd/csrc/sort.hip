@@ -5,7 +5,7 @@
 // Workgroup 0 (1024 threads) does the whole sort in LDS (sort_wg in
 // prologue.hpp: histogram, padded scan and block map, stable ballot-ranked
 // scatter); workgroups 1.. clear the requested region with 16-byte stores.
-// Larger pair counts use the three-launch variant further below.
+// Larger pair counts use the two-launch variant further below.
 #include "prologue.hpp"
 
 namespace moe {
@@ -21,13 +21,17 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(SortParams p) {
   sort_wg(p, p.ids, sm);
 }
 
-// ---- three-launch sort for large pair counts --------------------------------
-// A: per-chunk expert histograms (order-independent LDS atomics);
-// B: one workgroup scans the histograms over chunks per expert and over the
-//    padded expert counts, and writes counts, offsets, block map, sentinels and
-//    each chunk's base position per expert;
-// C: per chunk, the same ballot-match ranking as the single-workgroup sort
-//    places every pair at base[chunk][e] + (rank within the chunk).
+// ---- two-launch sort for large pair counts -----------------------------------
+// A: per-chunk expert histograms (order-independent LDS atomics), one
+//    workgroup per chunk of 1024 pairs;
+// B: one workgroup per chunk again.  Each reads every chunk's histogram
+//    (a few thousand words from L2) and derives what it needs itself: the
+//    experts' totals, the padded exclusive scan over experts, and its own
+//    chunk's base per expert (offset + the counts of the chunks before it);
+//    then it places its pairs with the ballot-match ranking of the
+//    single-workgroup sort.  The bookkeeping (counts, offsets, block map,
+//    padding sentinels) is spread over all the workgroups.  No workgroup
+//    waits for another, so there is no serial scan launch in between.
 constexpr int kChunk = kSortThreads;  // pairs per chunk (one per thread)
 
 __global__ __launch_bounds__(kSortThreads) void sort_count_kernel(SortParams p) {
@@ -46,37 +50,42 @@ __global__ __launch_bounds__(kSortThreads) void sort_count_kernel(SortParams p) 
     p.chunk_base[(size_t)blockIdx.x * p.n_experts + e] = s_count[e];
 }
 
-__global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(SortParams p) {
-  __shared__ int s_count[kMaxSortExperts];
+__global__ __launch_bounds__(kSortThreads) void sort_place_kernel(SortParams p) {
+  __shared__ int s_wave[kSortWaves][kMaxSortExperts];
+  __shared__ int s_tot[kMaxSortExperts];
+  __shared__ int s_pre[kMaxSortExperts];
   __shared__ int s_off[kMaxSortExperts + 1];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int nE = p.n_experts, BM = p.block_m;
   const int nchunk = (p.P + kChunk - 1) / kChunk;
-  // per-expert totals: every (chunk, expert) count once, all loads in flight
-  // together (coalesced over experts), summed with LDS atomics
-  for (int e = tid; e < nE; e += kSortThreads) s_count[e] = 0;
-  __syncthreads();
-  const int ncount = nchunk * nE;
-  for (int base = 0; base < ncount; base += 8 * kSortThreads) {
-    int v[8];
+  const int c = blockIdx.x;
+  for (int i = tid; i < kSortWaves * kMaxSortExperts; i += kSortThreads) (&s_wave[0][0])[i] = 0;
+
+  // 1. per expert: the total over all chunks and the sum over chunks < c
+  //    (16 chunks' loads in flight at a time, coalesced over experts)
+  for (int e = tid; e < nE; e += kSortThreads) {
+    int tot = 0, pre = 0;
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      int v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kSortThreads + tid;
-      v[u] = i < ncount ? p.chunk_base[i] : 0;
-    }
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < nchunk ? p.chunk_base[(size_t)(c0 + u) * nE + e] : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kSortThreads + tid;
-      if (i < ncount && v[u]) atomicAdd(&s_count[i % nE], v[u]);
+      for (int u = 0; u < 16; ++u) {
+        tot += v[u];
+        pre += (c0 + u < c) ? v[u] : 0;
+      }
     }
+    s_tot[e] = tot;
+    s_pre[e] = pre;
   }
   __syncthreads();
+  // 2. padded exclusive scan over the experts (wave 0)
   if (wv == 0) {
     int carry = 0;
     for (int base = 0; base < nE; base += kWave) {
       const int e = base + lane;
-      const int c = e < nE ? s_count[e] : 0;
-      const int pc = (c + BM - 1) / BM * BM;
+      const int cnt = e < nE ? s_tot[e] : 0;
+      const int pc = (cnt + BM - 1) / BM * BM;
       int incl = pc;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -91,34 +100,32 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(SortParams p) {
   __syncthreads();
   const int total = s_off[nE];
   const int nblk = total / BM;
-  for (int e = tid; e < nE; e += kSortThreads) {
-    p.counts[e] = s_count[e];
-    p.offsets[e] = s_off[e];
-    // chunk bases: the expert's offset plus the exclusive prefix of its counts
-    // over the chunks, 16 chunks' loads in flight at a time
-    int run = s_off[e];
-    for (int c0 = 0; c0 < nchunk; c0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = c0 + u < nchunk ? p.chunk_base[(size_t)(c0 + u) * nE + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (c0 + u < nchunk) p.chunk_base[(size_t)(c0 + u) * nE + e] = run;
-        run += v[u];
-      }
+
+  // 3. bookkeeping, spread over the workgroups (global thread index gi)
+  const long long gi = (long long)c * kSortThreads + tid;
+  const long long gstride = (long long)nchunk * kSortThreads;
+  if (c == 0) {
+    for (int e = tid; e < nE; e += kSortThreads) {
+      p.counts[e] = s_tot[e];
+      p.offsets[e] = s_off[e];
     }
-    for (int i = s_off[e] + s_count[e]; i < s_off[e + 1]; ++i) p.sorted[i] = p.P;
+    if (tid == 0) {
+      p.offsets[nE] = total;
+      *p.num_blocks = nblk;
+    }
   }
-  if (tid == 0) {
-    p.offsets[nE] = total;
-    *p.num_blocks = nblk;
+  for (long long i = gi; i < (long long)nE * BM; i += gstride) {  // padding slots of each expert
+    const int e = (int)(i / BM), j = (int)(i % BM);
+    const int at = s_off[e] + s_tot[e] + j;
+    if (at < s_off[e + 1]) p.sorted[at] = p.P;
   }
   const int max_blocks = p.capacity / BM;
-  for (int b = tid; b < max_blocks; b += kSortThreads) {
+  for (long long b = gi; b < max_blocks; b += gstride) {  // block -> expert
     int be = -1;
     if (b < nblk) {
-      int row = b * BM, lo = 0, hi = nE - 1;
-      while (lo < hi) {
+      const int row = (int)b * BM;
+      int lo = 0, hi = nE - 1;
+      while (lo < hi) {  // last e with off[e] <= row
         const int mid = (lo + hi + 1) / 2;
         if (s_off[mid] <= row) lo = mid; else hi = mid - 1;
       }
@@ -126,31 +133,27 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(SortParams p) {
     }
     p.block_expert[b] = be;
   }
-  for (int i = total + tid; i < p.capacity; i += kSortThreads) p.sorted[i] = p.P;
-}
+  for (long long i = total + gi; i < p.capacity; i += gstride) p.sorted[i] = p.P;  // unused tail
 
-__global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortParams p) {
-  __shared__ int s_wave[kSortWaves][kMaxSortExperts];
-  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-  for (int i = tid; i < kSortWaves * kMaxSortExperts; i += kSortThreads) (&s_wave[0][0])[i] = 0;
-  const int pi = blockIdx.x * kChunk + tid;
+  // 4. this chunk's pairs: base = offset + earlier chunks, then the waves
+  //    before this one, then the rank among equal experts in the wave
+  const int pi = c * kChunk + tid;
   const bool valid = pi < p.P;
   const int e = valid ? p.ids[pi] : 0;
   uint64_t peers = __ballot(valid);
 #pragma unroll
   for (int bit = 0; bit < 10; ++bit) {
-    const bool b = (e >> bit) & 1;
-    const uint64_t bal = __ballot(b);
-    peers &= b ? bal : ~bal;
+    const bool bb = (e >> bit) & 1;
+    const uint64_t bal = __ballot(bb);
+    peers &= bb ? bal : ~bal;
   }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int rank = __popcll(peers & lt_mask);
   const int leader = valid ? (__ffsll((unsigned long long)peers) - 1) : -1;
-  __syncthreads();
   if (valid && lane == leader) s_wave[wv][e] = __popcll(peers);
   __syncthreads();
   if (valid) {
-    int pos = p.chunk_base[(size_t)blockIdx.x * p.n_experts + e] + rank;
+    int pos = s_off[e] + s_pre[e] + rank;
     for (int w = 0; w < wv; ++w) pos += s_wave[w][e];
     p.sorted[pos] = pi;
   }
@@ -169,8 +172,7 @@ hipError_t launch_sort(const SortParams& p, hipStream_t s) {
   }
   const int nchunk = (p.P + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(sort_count_kernel, dim3(nchunk + (int)zblocks), dim3(kSortThreads), 0, s, p);
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kSortThreads), 0, s, p);
-  hipLaunchKernelGGL(sort_scatter_kernel, dim3(nchunk), dim3(kSortThreads), 0, s, p);
+  hipLaunchKernelGGL(sort_place_kernel, dim3(nchunk), dim3(kSortThreads), 0, s, p);
   return hipGetLastError();
 }
 
