@@ -52,9 +52,9 @@ EXPECTED = {
                              "gemm_tile_accum_kernel"],
     # aux stream: shared stage 1 and STORE stage 2 (a8w8: clear of the shared
     # row maxima, row quantisation); main: ..., routed stage 2 last
-    ("sorted", "aux", 64): ["gemm_tile_kernel<1, 1, 4>", "gemm_tile_kernel<1, 2, 4>", "gemm_tile_accum_kernel"],
-    ("a8w8", "aux", 64): ["fill_zero_kernel", "gemm_tile_kernel<3, 1, 4>", "quant_rows_kernel",
-                          "gemm_tile_kernel<3, 2, 4>", "gemm_tile_accum_kernel"],
+    ("sorted", "aux", 64): ["gemm_tile_kernel<1, 1, 4,", "gemm_tile_kernel<1, 2, 4,", "gemm_tile_accum_kernel"],
+    ("a8w8", "aux", 64): ["fill_zero_kernel", "gemm_tile_kernel<3, 1, 4,", "quant_rows_kernel",
+                          "gemm_tile_kernel<3, 2, 4,", "gemm_tile_accum_kernel"],
 }
 
 
