@@ -5,7 +5,7 @@ stage 2 with the shared-expert addend) over one batch of seeded synthetic
 inputs already resident in HBM.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload a8w8_large]
-                    [--mode auto|pseudo|aux|best] [--graph] [--no-cpu-baseline]
+                    [--mode auto|pseudo|aux|best] [--graph] [--router] [--no-cpu-baseline]
                     [--copy-calibration MIB]
 
 Per-kernel durations come from HIP events that the layer records between its
@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated per step (0 = auto)")
     ap.add_argument("--block-m", type=int, default=0, help="rows per sorted block (0 = automatic)")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays of the forward")
+    ap.add_argument("--router", action="store_true",
+                    help="give the layer its router projection (N(0, 1/H) weights) instead of logits, so the "
+                         "router GEMM runs in the routing launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
@@ -177,6 +180,8 @@ def main():
 
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.workload]
+    if args.router:
+        cfg = cfg.replace(router_std=float(cfg.H) ** -0.5)
     inp = workloads.generate(cfg, device=dev)
     wbytes = workloads.bytes_per_weight(cfg.fmt) * 3.0 * cfg.H * (cfg.E * cfg.I + cfg.I_s)
     copies = args.copies or max(1, min(6, int(np.ceil(3 * 256e6 / wbytes))))
@@ -243,13 +248,20 @@ def main():
     # routing result of the timed workload (for the algorithmic byte count)
     ids = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=dev)
     w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=dev)
-    m.moe_route(inp["logits"], ids, w, topk=cfg.topk, bias=inp.get("bias"), n_group=cfg.n_group,
+    logits = inp["logits"]
+    if logits is None:  # router-GEMM mode: the same logits the layer computed
+        logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+        m.moe_router_logits(inp["x"], inp["router_w"], logits, x_row_scale=inp.get("x_scale"))
+    m.moe_route(logits, ids, w, topk=cfg.topk, bias=inp.get("bias"), n_group=cfg.n_group,
                 topk_group=cfg.topk_group, group_score_topk=cfg.group_score_topk,
                 score=m.MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else m.MOE_SCORE_SOFTMAX,
                 renormalize=cfg.renormalize, routed_scaling_factor=cfg.routed_scaling_factor)
     torch.cuda.synchronize()
     m_pseudo = cfg.n_pseudo if best == "pseudo" else 0
     flops, byt, s1, s2, active = algorithmic(cfg, ids.cpu().numpy(), m_pseudo)
+    if args.router:  # the router GEMM: its FLOPs and its weights once
+        flops += 2.0 * cfg.T * cfg.E * cfg.H
+        byt += cfg.E * cfg.H * (4 if cfg.fmt == "f32" else 2)
     rec = {
         "metric": METRIC,
         "value": cfg.T / (ms * 1e-3),
@@ -265,7 +277,7 @@ def main():
         "data": "synthetic (seeded; random-init weights of the workload's shapes)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "I_s": cfg.I_s,
                    "topk": cfg.topk, "score": cfg.score, "shared_mode": best, "weight_copies": copies,
-                   "graph": bool(args.graph), "active_experts": active},
+                   "graph": bool(args.graph), "router_gemm": bool(args.router), "active_experts": active},
         "layer": {"tflops": flops / (ms * 1e-3) / 1e12, "gbps": byt / (ms * 1e-3) / 1e9,
                   "frac_mfma": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.fmt],
                   "frac_hbm": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

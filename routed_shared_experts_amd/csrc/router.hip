@@ -9,33 +9,40 @@
 // PR 65207, "Purpose", commit 1) -- to the router projection itself, so the
 // logits never travel through HBM between two launches.
 //
-// Mapping.  A workgroup of four waves owns 64 consecutive tokens, wave w the
-// 16 tokens 16 w ..; every wave computes all E_pad = 16 NT experts of its
-// tokens (NT 16x16 MFMA tiles, experts = rows of the A operand, tokens =
-// columns).  Per K tile (128 bytes of a router-weight row: 64 bf16 or 32
-// fp32 elements), the E_pad weight rows are staged once in LDS
-// (XOR-swizzled 16-byte chunks, rows past E read as zero) and shared by the
-// four waves; each wave reads its 16 token rows straight into B-operand
-// registers (e4m3 activations are widened to bf16 on the way, exactly).  The
-// fp32 accumulators are multiplied by the token's scale (e4m3 input), written
-// to the logits output and to LDS, and route_token reads them from there.
+// Mapping.  A workgroup of four waves owns 16 consecutive tokens and all
+// E_pad = 16 NT experts: wave w computes the tokens against every fourth
+// 16-expert MFMA tile starting at w (experts = rows of the A operand, tokens
+// = columns).
+// Per K tile (128 bytes of a router-weight row: 64 bf16 or 32 fp32
+// elements) the E_pad weight rows are staged once in LDS (XOR-swizzled
+// 16-byte chunks, rows past E read as zero) for the four waves, in two
+// buffers: the next tile's rows and token fragments are loaded into
+// registers while the current one is multiplied, so one barrier per tile
+// remains and the load latency is hidden.  Token rows go straight into
+// B-operand registers (e4m3 activations are widened to bf16 on the way,
+// exactly).  The fp32 accumulators are multiplied by the token's scale (e4m3
+// input), written to the logits output and to LDS, and route_token then
+// routes the workgroup's tokens from there, four per wave.  (Measured on
+// MI355X: 64-token workgroups read the router weights a quarter as often
+// but were slower -- 187 against 158 us for the logits alone at T = 8192,
+// H = 7168, E = 256 -- and route 16 tokens per wave in sequence.)
 #include "gemm_common.hpp"
 #include "prologue.hpp"
 
 namespace moe {
 
-constexpr int kRtTokens = 64;
 constexpr int kRtThreads = 256;
+constexpr int kRtTokens = 16;  // tokens per workgroup
 
 template <int NT>
 struct RouterSmem {
   static constexpr int EP = 16 * NT;
-  static constexpr int kTile = EP * 128;            // one K tile of the router weights
-  static constexpr int kLogits = kRtTokens * EP * 4;  // the block's logits, fp32
+  static constexpr int kTiles = 2 * EP * 128;            // two K tiles of the router weights
+  static constexpr int kLogits = kRtTokens * EP * 4;     // the block's logits, fp32
   union {
-    uint8_t w[kTile];
+    uint8_t w[2][EP * 128];
     float logit[kRtTokens * EP];
-    uint8_t raw[kTile > kLogits ? kTile : kLogits];
+    uint8_t raw[kTiles > kLogits ? kTiles : kLogits];
   };
   float sel[kRtThreads / kWave][EP];
   float val[kRtThreads / kWave][EP];
@@ -62,80 +69,114 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 template <int XF, int NT, int NPL>
 __global__ __launch_bounds__(kRtThreads) void router_kernel(RouterParams g, RouteParams rp) {
   constexpr int EP = 16 * NT;
+  constexpr int BT = kRtTokens;
+  constexpr int NTW = NT / 4;            // expert tiles per wave
+  constexpr int CPT = EP * 8 / kRtThreads;  // weight chunks per thread per K tile
   constexpr int FMT = XF == 0 ? FMT_F32 : FMT_BF16;
   constexpr int XB = XF == 0 ? 4 : (XF == 1 ? 2 : 1);  // bytes per x element
   constexpr int KE = XF == 0 ? 32 : 64;                // elements per K tile
+  static_assert(NT % 4 == 0 && CPT >= 1, "expert tiles must split over the waves");
   __shared__ __attribute__((aligned(16))) RouterSmem<NT> sm;
 
-  const int nblk = (g.T + kRtTokens - 1) / kRtTokens;
+  const int nblk = (g.T + BT - 1) / BT;
   if ((int)blockIdx.x >= nblk) {
     clear_region(rp.zero_ptr, rp.zero_vec, nblk);
     return;
   }
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int g4 = lane / 16, r = lane % 16;
-  const int t0 = blockIdx.x * kRtTokens;
-  const int tok = t0 + 16 * wv + r;
+  const int t0 = blockIdx.x * BT;
+  const int tok = t0 + r;
   const bool tok_ok = tok < g.T;
   const size_t wrow = (size_t)g.H * (XF == 0 ? 4 : 2);  // bytes per router-weight row
   const uint8_t* xrow = static_cast<const uint8_t*>(g.x) + (size_t)(tok_ok ? tok : 0) * g.H * XB;
+  const uint8_t* wbase = static_cast<const uint8_t*>(g.w);
 
-  f32x4 acc[NT];
+  uint4 wr[CPT];
+  auto load_w = [&](int kt) {
 #pragma unroll
-  for (int et = 0; et < NT; ++et) acc[et] = f32x4{0, 0, 0, 0};
-  const int nk = g.H / KE;
-  for (int kt = 0; kt < nk; ++kt) {
-    // the E_pad weight rows of this K tile -> LDS
-#pragma unroll 4
-    for (int i = tid; i < EP * 8; i += kRtThreads) {
+    for (int u = 0; u < CPT; ++u) {
+      const int i = tid + kRtThreads * u;
       const int row = i / 8, c = i % 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < g.E) v = ld16(static_cast<const uint8_t*>(g.w) + (size_t)row * wrow + (size_t)kt * 128 + 16 * c);
-      *reinterpret_cast<uint4*>(sm.w + swz(row, c)) = v;
+      wr[u] = row < g.E ? ld16(wbase + (size_t)row * wrow + (size_t)kt * 128 + 16 * c) : make_uint4(0, 0, 0, 0);
     }
-    // this lane's B operand: token tok, chunks g4 and 4 + g4 of the K tile
-    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-    if (tok_ok) {
-      if constexpr (XF == 2) {
-        const uint8_t* xp = xrow + (size_t)kt * 64;
-        const uint2 c0 = *reinterpret_cast<const uint2*>(xp + 8 * g4);
-        const uint2 c1 = *reinterpret_cast<const uint2*>(xp + 32 + 8 * g4);
-        b0 = e4m3x8_to_bf16(c0.x, c0.y);
-        b1 = e4m3x8_to_bf16(c1.x, c1.y);
-      } else {
-        const uint8_t* xp = xrow + (size_t)kt * 128;
-        b0 = ld16(xp + 16 * g4);
-        b1 = ld16(xp + 64 + 16 * g4);
-      }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int i = tid + kRtThreads * u;
+      *reinterpret_cast<uint4*>(&sm.w[buf][swz(i / 8, i % 8)]) = wr[u];
+    }
+  };
+  // this lane's B operand: token tok, chunks g4 and 4 + g4 of K tile kt
+  auto load_x = [&](int kt, uint4& b0, uint4& b1) {
+    b0 = make_uint4(0, 0, 0, 0);
+    b1 = make_uint4(0, 0, 0, 0);
+    if (!tok_ok) return;
+    if constexpr (XF == 2) {
+      const uint8_t* xp = xrow + (size_t)kt * 64;
+      const uint2 c0 = *reinterpret_cast<const uint2*>(xp + 8 * g4);
+      const uint2 c1 = *reinterpret_cast<const uint2*>(xp + 32 + 8 * g4);
+      b0 = e4m3x8_to_bf16(c0.x, c0.y);
+      b1 = e4m3x8_to_bf16(c1.x, c1.y);
+    } else {
+      const uint8_t* xp = xrow + (size_t)kt * 128;
+      b0 = ld16(xp + 16 * g4);
+      b1 = ld16(xp + 64 + 16 * g4);
+    }
+  };
+
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  const int nk = g.H / KE;
+  uint4 b0, b1;
+  load_w(0);
+  load_x(0, b0, b1);
+  store_w(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    uint4 n0, n1;
+    if (more) {
+      load_w(kt + 1);
+      load_x(kt + 1, n0, n1);
+    }
+    const uint8_t* wt = sm.w[kt & 1];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int et = wv + 4 * i;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(wt + swz(16 * et + r, g4));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(wt + swz(16 * et + r, 4 + g4));
+      mfma_tile<FMT>(acc[i], a0, a1, b0, b1, 0, 0);
+    }
+    if (more) {
+      store_w((kt + 1) & 1);  // its buffer was last read before the previous barrier
+      b0 = n0;
+      b1 = n1;
     }
     __syncthreads();
-#pragma unroll
-    for (int et = 0; et < NT; ++et) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(sm.w + swz(16 * et + r, g4));
-      const uint4 a1 = *reinterpret_cast<const uint4*>(sm.w + swz(16 * et + r, 4 + g4));
-      mfma_tile<FMT>(acc[et], a0, a1, b0, b1, 0, 0);
-    }
-    __syncthreads();  // the next tile rewrites the weights
   }
 
-  // logits of token 16 wv + r: experts 16 et + 4 g4 + v
+  // logits of token r: experts 16 et + 4 g4 + v (the weight buffers
+  // are dead now: the union's logits overwrite them after the last barrier)
   const float xs = (XF == 2 && tok_ok) ? g.x_scale[tok] : 1.0f;
 #pragma unroll
-  for (int et = 0; et < NT; ++et)
+  for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int e = 16 * et + 4 * g4 + v;
-      const float l = acc[et][v] * xs;
-      sm.logit[(16 * wv + r) * EP + e] = l;
+      const int e = 16 * (wv + 4 * i) + 4 * g4 + v;
+      const float l = acc[i][v] * xs;
+      sm.logit[r * EP + e] = l;
       if (tok_ok && e < g.E) g.logits[(size_t)tok * g.E + e] = l;
     }
   if (!rp.do_route) return;
   __syncthreads();
-  // routing (+ gate dot, + MX quantisation of x) of the wave's 16 tokens
-  for (int i = 0; i < 16; ++i) {
-    const int t = t0 + 16 * wv + i;
+  // routing (+ gate dot, + MX quantisation of x): token i of the block by wave i % 4
+  for (int i = wv; i < BT; i += kRtThreads / kWave) {
+    const int t = t0 + i;
     if (t >= g.T) break;
-    route_token<NPL>(rp, t, lane, sm.sel[wv], sm.val[wv], &sm.logit[(16 * wv + i) * EP]);
+    route_token<NPL>(rp, t, lane, sm.sel[wv], sm.val[wv], &sm.logit[i * EP]);
   }
 }
 
