@@ -318,7 +318,7 @@ moe_status moe_quant_mx(const void* x, int32_t T, int32_t H, uint8_t* codes,
 int32_t moe_sort_capacity(int32_t T, int32_t k_total, int32_t n_experts, int32_t block_m);
 
 /* Device scratch bytes moe_sort_tokens can use to sort large pair counts
- * with three launches instead of one workgroup (0 when it would not use it).
+ * with two launches instead of one workgroup (0 when it would not use it).
  * Host-only. */
 size_t moe_sort_scratch_bytes(int32_t T, int32_t k_total, int32_t n_experts);
 
