@@ -193,8 +193,9 @@ typedef struct {
   int32_t activation; /* moe_activation of routed and shared experts (0 = SILU) */
   /* optional router projection [E][H], row-major (F32 when x is F32, else
    * BF16; F32 accumulation): when not NULL the layer computes the router
-   * logits x . router_w^T itself, in the routing launch (A8W8: from the
-   * dequantised codes, code * x_row_scale), and logits is not read (may be
+   * logits x . router_w^T itself in the prologue -- a GEMM launch before the
+   * routing launch, or for F32 x one launch that also routes (A8W8: from the
+   * dequantised codes, code * x_row_scale) -- and logits is not read (may be
    * NULL) */
   const void* router_w;
 } moe_forward_args;
@@ -294,8 +295,12 @@ moe_status shared_gate_dot(const void* x, int32_t x_dtype, const void* g, int32_
                            hipStream_t stream);
 
 /* Router logits l = x . router_w^T (the projection in front of the routing
- * of vLLM PR 65207, "Purpose", commit 1; the same matrix-core kernel the
- * fused prologue of moe_forward runs, without the routing).
+ * of vLLM PR 65207, "Purpose", commit 1; the same matrix-core kernel
+ * moe_forward runs for the same shapes, without the routing: for BF16 and
+ * FP8_E4M3 x a tiled GEMM of 128 tokens x 64 experts per workgroup, whose
+ * logits the forward then routes in a second launch; for F32 x the kernel of
+ * the forward's fused prologue).  A forward fed these logits therefore routes
+ * exactly as one given the router weights.
  * x [T][H] in x_dtype: F32 (router_w F32), BF16 (router_w BF16) or FP8_E4M3
  * codes with x_row_scale [T] fp32 (router_w BF16; l = scale_t * codes . w);
  * router_w [E][H] row-major; logits [T][E] fp32 out.  H % 64 == 0 (% 32 for
