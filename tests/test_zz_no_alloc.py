@@ -21,6 +21,8 @@ CASES = {
     # sorted 64-row blocks, tiled kernels, a8w8 row quantisation
     "a8w8": LC("noalloc_a8w8", T=200, H=512, E=16, I=256, I_s=256, topk=4, score="sigmoid", n_group=4,
                topk_group=2, fmt="a8w8", gated=False, logits="zipf", zipf_s=1.2),
+    # router weights instead of logits: the logits GEMM writes into the scratch
+    "router": LC("noalloc_router", T=150, H=512, E=40, I=128, I_s=128, topk=4, fmt="bf16", router_std=0.05),
 }
 
 
