@@ -51,6 +51,8 @@ SHAPES = {
     "t1100_e257": LC("rt_t1100_e257", T=1100, H=1024, E=257, I=128, I_s=0, topk=4, fmt="bf16", router_std=0.03),
     "t2049_e512_a8w8": LC("rt_t2049_e512_a8w8", T=2049, H=640, E=512, I=128, I_s=0, topk=8, fmt="a8w8",
                           router_std=0.03),
+    # fp32 activations take the one-launch kernel: many workgroups of it
+    "t600_f32": LC("rt_t600_f32", T=600, H=256, E=100, I=64, I_s=0, topk=4, fmt="f32", router_std=0.1),
     # one token, one 64-element K tile (fewer K tiles than loads in flight)
     "t1_h64": LC("rt_t1_h64", T=1, H=64, E=8, I=64, I_s=0, topk=2, fmt="bf16", router_std=0.1),
     "t5_h128_e65_a8w8": LC("rt_t5_h128_e65_a8w8", T=5, H=128, E=65, I=64, I_s=0, topk=3, fmt="a8w8",
